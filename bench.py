@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of a transformer layer over a paged KV pool.
+
+Default workload: the bf16 7B-class batched decode layer (hidden 3584, 28 q /
+4 kv heads, head_dim 128, FFN 18944, 768 rows, contexts 128 + U{1..128} with a
+shared 2-page prompt prefix).  A step is one pass of the whole path: QKV
+projection, append of each row's key/value, paged attention, output projection
++ residual, gate/up projection + SiLU, down projection + residual.
+
+Prints one JSON line.  `value` = algorithmic HBM bytes of the step / measured
+step time (GB/s); the per-stage breakdown and the dominant kernel's roofline
+are measured with HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for p in (ROOT, os.path.join(ROOT, "tests")):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="7b-b768-prefix-bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--family", type=int, default=None, help="override the projection family")
+    return ap.parse_args()
+
+
+def step_bytes(w, elem):
+    """Algorithmic bytes of one step, per stage (what the method must move)."""
+    import numpy as np
+    B, D, nq, nkv, d, F = w.n_rows, w.hidden, w.n_q, w.n_kv, w.head_dim, w.ffn
+    sw, skv, sa = elem[w.w_dtype], elem[w.kv_dtype], elem[w.act_dtype]
+    nqkv = (nq + 2 * nkv) * d
+    fp8 = w.w_dtype == 2
+    # unique (physical page, slot) pairs read by attention: slots < L of every row's pages
+    seen = {}
+    for r in range(B):
+        s, L = int(w.seq[r]), int(w.pos[r]) + 1
+        for lp in range((L + 31) // 32):
+            pg = int(w.tables[s][lp])
+            n = min(32, L - 32 * lp)
+            seen[pg] = max(seen.get(pg, 0), n)
+    kv_tokens = sum(seen.values())
+    pages_touched = sum((int(p) + 32) // 32 for p in w.pos)
+    xin = 1 if fp8 else sa  # projection input bytes per element (fp8 codes or act dtype)
+    st = {}
+    st["cast"] = 0 if fp8 or w.act_dtype == 0 else B * D * (4 + 2)
+    st["qkv"] = nqkv * D * sw + B * D * (4 if fp8 else xin) + B * nqkv * sa
+    st["append"] = B * 2 * nkv * d * skv + B * 2 * nkv * d * sa
+    st["attention"] = (kv_tokens * 2 * nkv * d * skv + B * nq * d * (sa + sa) + 4 * pages_touched + 8 * B)
+    st["wo"] = D * nq * d * sw + B * nq * d * sa + B * D * 4 * 2 + (0 if fp8 else B * D * 2)
+    if F:
+        st["gate_up"] = 2 * F * D * sw + B * D * (4 if fp8 else 2) + B * F * sa
+        st["down"] = D * F * sw + B * F * sa + B * D * 4 * 2
+    flops = {"qkv": 2 * B * nqkv * D, "wo": 2 * B * D * nq * d}
+    if F:
+        flops["gate_up"] = 2 * B * 2 * F * D
+        flops["down"] = 2 * B * D * F
+    flops["attention"] = 4 * nq * d * int(sum(int(p) + 1 for p in w.pos))
+    return st, flops, kv_tokens
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every box here has one MI355X and the path has no "
+              f"multi-GPU leg in this build (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_attn_amd as pkd
+    import workloads as wl
+    import gpu_harness as H
+
+    torch.cuda.set_device(0)
+    kw = {} if args.family is None else {"family": args.family}
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    w = wl.make(args.workload, "cuda", **kw)
+    pool = H.GpuPool(w)
+    layer = H.GpuLayer(w)
+    L = layer.layer
+    B, D, nq, nkv, d, F = w.n_rows, w.hidden, w.n_q, w.n_kv, w.head_dim, w.ffn
+    stream = torch.cuda.current_stream()
+    s_t, p_t = H.rows_tensors(w.seq, w.pos)
+    rows = pkd.make_rows(s_t, p_t)
+    x = w.x.contiguous()
+    y = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    ws = H.aligned_empty(pkd.pkd_step_workspace_bytes(L, pool.handle, B))
+
+    # ---------------------------------------------------------------- whole step
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        pkd.decode_step(L, pool.handle, rows, x, y, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        pkd.decode_step(L, pool.handle, rows, x, y, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    pkd.pkd_pool_check(pool.handle)
+    print(f"[bench] decode_step {ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- per stage
+    # The same kernels with the same shapes, launched stage by stage through the
+    # public entry points, with events between stages on the same stream.
+    act = w.act_dtype
+    fp8 = w.w_dtype == 2
+    ebytes = {0: 4, 1: 2, 2: 1}
+    nqkv = (nq + 2 * nkv) * d
+    tdt = torch.float32 if act == 0 else torch.int16
+    qkv = torch.empty((B, nqkv), dtype=tdt, device="cuda")
+    att = torch.empty((B, nq * d), dtype=tdt, device="cuda")
+    h = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    hb = torch.empty((B, D), dtype=torch.int16, device="cuda")
+    xb = x.to(torch.bfloat16).view(torch.int16)
+    a_ = torch.empty((B, max(F, 1)), dtype=tdt, device="cuda")
+    pws = max(pkd.pkd_gemv_workspace_bytes(m, B) for m in (L.w_qkv, L.w_o, L.w_gate_up, L.w_down))
+    pws = H.aligned_empty(pws) if pws else None
+    aws = H.aligned_empty(pkd.pkd_attn_workspace_bytes(pool.handle, nq, B))
+    es = ebytes[act]
+    stages = []
+
+    def st_qkv():
+        xin, xdt = (x, 0) if (fp8 or act == 0) else (xb, 1)
+        pkd.gemv_rows(L.w_qkv, xin, xdt, B, qkv, act, ws=pws)
+
+    def st_append_attn():
+        # q, k_new, v_new as separate contiguous tensors (paged_attn_decode takes dense rows)
+        pkd.paged_attn_decode(pool.handle, rows, nq, q_c, k_c, v_c, att, act, aws)
+
+    def st_wo():
+        pkd.gemv_rows(L.w_o, att, act, B, h, 0, residual=x, y_bf16=(None if (fp8 or act == 0) else hb), ws=pws)
+
+    def st_gu():
+        hin, hdt = (h, 0) if (fp8 or act == 0) else (hb, 1)
+        pkd.gemv_rows(L.w_gate_up, hin, hdt, B, a_, act, silu_pair=True, ws=pws)
+
+    def st_down():
+        pkd.gemv_rows(L.w_down, a_, act, B, y, 0, residual=h, ws=pws)
+
+    st_qkv()
+    torch.cuda.synchronize()
+    q3 = qkv.view(B, nq + 2 * nkv, d)
+    q_c = q3[:, :nq].contiguous()
+    k_c = q3[:, nq:nq + nkv].contiguous()
+    v_c = q3[:, nq + nkv:].contiguous()
+    stages = [("qkv", st_qkv), ("attention", st_append_attn), ("wo", st_wo)]
+    if F:
+        stages += [("gate_up", st_gu), ("down", st_down)]
+    for _ in range(args.warmup):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        for i, (_, f) in enumerate(stages):
+            f()
+            evs[k][i + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_us = {}
+    for i, (name, _) in enumerate(stages):
+        stage_us[name] = float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)])) * 1e3
+    sbytes, sflops, kv_tokens = step_bytes(w, ebytes)
+    sbytes_m = dict(sbytes)
+    sbytes_m["attention"] = sbytes["attention"] + sbytes["append"]
+    total_bytes = sum(sbytes.values())
+    kernels = {}
+    for name, us in stage_us.items():
+        kb = sbytes_m.get(name, 0)
+        fl = sflops.get(name, 0)
+        kernels[name] = {"us": round(us, 2), "bytes": int(kb), "GB_s": round(kb / us / 1e3, 1),
+                         "hbm_frac": round(kb / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "TFLOP_s": round(fl / us / 1e6, 1) if fl else None}
+    # dominant kernel: longest stage
+    dom = max(stage_us, key=stage_us.get)
+    dt = "fp8" if fp8 else "bf16"
+    fam = L.w_gate_up.family if F else L.w_qkv.family
+    if dom == "attention" or fam == 0:
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+        achieved = sbytes_m[dom] / stage_us[dom] / 1e3
+    else:
+        bound, unit = "mfma", "TFLOP/s"
+        peak = MFMA_PEAK_TFLOPS["bf16"] if (fam == 1 or not fp8) else MFMA_PEAK_TFLOPS["fp8"]
+        achieved = sflops[dom] / stage_us[dom] / 1e6
+    roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None}
+    value = total_bytes / (ms_step * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        nr = min(args.cpu_rows, B)
+        rws = np.arange(nr)
+        seqs = np.unique(w.seq[rws])
+        hk, hv = wl.history_lists(w, seqs)
+        hist = orc.History(hk, hv, w.kv_dtype, nkv, d)
+        lay = wl.layer_dict(w)
+        xs = w.x[:nr].cpu().numpy()
+        print(f"[bench] cpu baseline: oracle on {nr} rows, {orc.threads()} threads", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        orc.decode_step(lay, hist, w.seq[rws], w.pos[rws], xs)
+        t1 = time.perf_counter()
+        per_step = (t1 - t0) / nr * B
+        cpu = {"value": round(total_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": orc.threads(),
+               "kind": "oracle", "us_per_step": round(per_step * 1e6, 1),
+               "sample": f"fp64 oracle decode step of the first {nr} of {B} rows ({t1 - t0:.1f} s), "
+                         f"time per row x {B} rows"}
+
+    line = {
+        "metric": "decode-step us and achieved HBM GB/s (% of peak), paged attn + GEMV",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.w_dtype], "data": "synthetic",
+        "config": {"workload": w.name, "rows": B, "hidden": D, "q_heads": nq, "kv_heads": nkv, "head_dim": d,
+                   "ffn": F, "page_tokens": 32, "kv_tokens_unique": int(kv_tokens),
+                   "projection_family": int(fam), "parallelism": "none (1 GPU)"},
+        "step_bytes": int(total_bytes),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

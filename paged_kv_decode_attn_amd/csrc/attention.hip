@@ -1,0 +1,695 @@
+// Paged-attention decode for gfx950.
+//
+// What is computed (per row r at position p of sequence s, per query head h):
+// out = softmax over t in [0, p] of (q_h . K_t / sqrt(d)) applied to V_t, with
+// K_t, V_t fetched page by page through the sequence's block table and reduced
+// by an online softmax in fp32 ("Building an LLM runtime from scratch on NVIDIA
+// H100", section "Bug #1"; pages and block tables: "GPU inference engine
+// engineering", section "Batching without running out of cache").
+//
+// Work unit: one 64-lane wavefront per (row, kv head[, position chunk]).  The
+// G query heads sharing the kv head are the 16 columns of matrix-core tiles:
+//   S^T[32 tokens x 16 heads] = K_page[32 x d] . Q^T[d x 16]   (MFMA)
+//   O^T[d x 16 heads]        += V_page^T[d x 32] . P^T[32 x 16] (MFMA)
+// The pool layout (include/pkd.h) puts each 16-byte vector a lane loads exactly
+// where the matrix-core operand wants it, so a page arrives with fully
+// contiguous 1 KiB wave loads and no LDS round trip; the score accumulator of a
+// lane is already the P operand of the P.V product for the same lane, so the
+// softmax needs no data movement except the per-head max and sum across the
+// four 16-lane groups.  P enters the bf16 matrix core as a hi + lo pair of bf16
+// numbers so that the weights keep ~16 significant bits.
+//
+// Long contexts are split into fixed chunks of `attn_chunk_pages` pages (a pool
+// constant) merged in ascending chunk order afterwards ("llm-rs", section 4,
+// lesson 2).  Every reduction has a fixed order, so a row's result does not
+// depend on the batch ("GPU inference engine engineering", section "The same
+// bits in any batch").  Barriers: none; each wave works alone.
+
+#include <math.h>
+
+#include "common.h"
+
+namespace pkd {
+
+struct AttnParams {
+  const uint8_t* pages;
+  uint64_t page_stride;  // bytes per physical page: n_kv * 2 * block_bytes
+  uint32_t block_bytes;
+  const int32_t* table;
+  const int32_t* counts;
+  int32_t max_pages;
+  int32_t max_seqs;
+  uint32_t* err;
+  const int32_t* seq;
+  const int32_t* pos;
+  int32_t n_rows;
+  int32_t n_kv;
+  int32_t G;
+  const void* q;
+  int64_t q_stride;
+  void* out;
+  int32_t out_bf16;
+  int64_t out_stride;
+  float qk_scale;  // log2(e) / sqrt(d) * k_scale
+  float v_scale;
+  int32_t chunk_pages;
+  const int32_t* chunk_start;  // chunked: [n_rows + 1] first unit of each row
+  const int32_t* total_units;  // chunked: [1]
+  int32_t* counter;            // chunked: work counter
+  float* part_ml;              // chunked: [units * n_kv * G][2]  (m, l)
+  float* part_o;               // chunked: [units * n_kv * G][d]
+};
+
+// Per-KV-dtype geometry.  kvt: 0 f32, 1 bf16, 2 fp8.  NL = 16-byte loads per lane
+// for one K (or V) block of a page.
+template <int KVT, int D>
+struct Geo {
+  static constexpr int ES = KVT == 0 ? 4 : KVT == 1 ? 2 : 1;
+  static constexpr int NL = D * ES / 32;
+  static constexpr int NMT = D / 16;                // 16-dim output tiles
+  static constexpr int NQ = KVT == 0 ? D / 4 : D / 32;  // matrix-core k-steps per half page
+};
+
+template <int KVT, int D>
+using PageRegs = u32x4[Geo<KVT, D>::NL];
+template <int KVT, int D>
+using QRegs = u32x4[Geo<KVT, D>::NQ];
+template <int KVT, int D>
+using QFRegs = float[Geo<KVT, D>::NQ];
+template <int KVT, int D>
+using ORegs = f32x4_t[Geo<KVT, D>::NMT];
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Row validity and context length; sets the sticky error word on a bad row.
+__device__ __forceinline__ bool row_ok(const AttnParams& P, int s, int p, bool report) {
+  unsigned e = 0;
+  if (s < 0 || s >= P.max_seqs) e = kErrSeq;
+  else if (p < 0 || p >= kPage * P.counts[s]) e = kErrPos;
+  if (e && report && lane_id() == 0) atomicOr(P.err, e);
+  return e == 0;
+}
+
+// Loads the query registers (B operand of the score product) of kv head g.
+template <int KVT, int D>
+__device__ __forceinline__ void load_q(const AttnParams& P, int r, int g, QRegs<KVT, D>& qv,
+                                       QFRegs<KVT, D>& qf) {
+  using GE = Geo<KVT, D>;
+  const int l = lane_id(), grp = l >> 4, n = l & 15;
+  const bool live = n < P.G;
+  const int h = g * P.G + (live ? n : 0);
+  if constexpr (KVT == 0) {
+    const float* q = reinterpret_cast<const float*>(P.q) + (int64_t)r * P.q_stride + (int64_t)h * D;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      u32x4 v = live ? load16(reinterpret_cast<const uint8_t*>(q + 16 * i + 4 * grp)) : u32x4{0, 0, 0, 0};
+      qf[4 * i + 0] = __uint_as_float(v.x);
+      qf[4 * i + 1] = __uint_as_float(v.y);
+      qf[4 * i + 2] = __uint_as_float(v.z);
+      qf[4 * i + 3] = __uint_as_float(v.w);
+    }
+  } else {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(P.q) + (int64_t)r * P.q_stride + (int64_t)h * D;
+#pragma unroll
+    for (int s = 0; s < GE::NQ; ++s) {
+      // bf16 pool: step s covers dims 32s + 8grp; fp8 pool: step s = 2i + e covers 64i + 16grp + 8e
+      int c = KVT == 1 ? 32 * s + 8 * grp : 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
+      qv[s] = live ? load16(reinterpret_cast<const uint8_t*>(q + c)) : u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// Scores of one page: S[a][i] = q_n . K[16a + 4grp + i] (unscaled), a = half page.
+template <int KVT, int D>
+__device__ __forceinline__ void page_scores(const PageRegs<KVT, D>& kr, const QRegs<KVT, D>& qv,
+                                            const QFRegs<KVT, D>& qf, f32x4_t (&S)[2]) {
+  using GE = Geo<KVT, D>;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KVT == 1) {
+#pragma unroll
+      for (int s = 0; s < GE::NQ; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[a * GE::NQ + s]), as_bf16x8(qv[s]), acc, 0, 0, 0);
+    } else if constexpr (KVT == 2) {
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) {
+        u32x4 w = kr[a * (D / 64) + i];
+        u32x2 b0 = fp8x4_to_bf16x4(w.x), b1 = fp8x4_to_bf16x4(w.y);
+        u32x2 b2 = fp8x4_to_bf16x4(w.z), b3 = fp8x4_to_bf16x4(w.w);
+        u32x4 lo = {b0.x, b0.y, b1.x, b1.y}, hi = {b2.x, b2.y, b3.x, b3.y};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), as_bf16x8(qv[2 * i]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), as_bf16x8(qv[2 * i + 1]), acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        u32x4 w = kr[a * (D / 16) + i];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.x), qf[4 * i + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.y), qf[4 * i + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.z), qf[4 * i + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.w), qf[4 * i + 3], acc, 0, 0, 0);
+      }
+    }
+    S[a] = acc;
+  }
+}
+
+// Zeroes the V elements of tokens at or past the context end (0 * NaN would
+// poison the product otherwise).  valid[a][i] for token 16a + 4grp + i.
+template <int KVT, int D>
+__device__ __forceinline__ void mask_v(PageRegs<KVT, D>& vr, const bool (&valid)[2][4]) {
+  using GE = Geo<KVT, D>;
+  if constexpr (KVT == 1) {
+    // dword w holds elements 2w, 2w + 1 = tokens (a = w / 2, i = 2(w % 2) + {0, 1})
+    unsigned m[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      m[w] = (valid[w >> 1][2 * (w & 1)] ? 0xffffu : 0u) | (valid[w >> 1][2 * (w & 1) + 1] ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int j = 0; j < GE::NL; ++j) {
+      vr[j].x &= m[0]; vr[j].y &= m[1]; vr[j].z &= m[2]; vr[j].w &= m[3];
+    }
+  } else if constexpr (KVT == 2) {
+    unsigned m[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+      m[a] = (valid[a][0] ? 0xffu : 0u) | (valid[a][1] ? 0xff00u : 0u) | (valid[a][2] ? 0xff0000u : 0u) |
+             (valid[a][3] ? 0xff000000u : 0u);
+#pragma unroll
+    for (int j = 0; j < GE::NL; ++j) {
+      vr[j].x &= m[0]; vr[j].y &= m[1]; vr[j].z &= m[0]; vr[j].w &= m[1];
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int mt = 0; mt < GE::NMT; ++mt) {
+        u32x4& v = vr[a * GE::NMT + mt];
+        v.x = valid[a][0] ? v.x : 0u;
+        v.y = valid[a][1] ? v.y : 0u;
+        v.z = valid[a][2] ? v.z : 0u;
+        v.w = valid[a][3] ? v.w : 0u;
+      }
+  }
+}
+
+// O^T += V^T . P^T for one page.  p[a][i] are the lane's softmax weights.
+template <int KVT, int D>
+__device__ __forceinline__ void page_pv(const PageRegs<KVT, D>& vr, const float (&p)[2][4],
+                                        ORegs<KVT, D>& O) {
+  using GE = Geo<KVT, D>;
+  if constexpr (KVT == 0) {
+#pragma unroll
+    for (int mt = 0; mt < GE::NMT; ++mt)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        u32x4 v = vr[a * GE::NMT + mt];
+        O[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), p[a][0], O[mt], 0, 0, 0);
+        O[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), p[a][1], O[mt], 0, 0, 0);
+        O[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), p[a][2], O[mt], 0, 0, 0);
+        O[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), p[a][3], O[mt], 0, 0, 0);
+      }
+  } else {
+    // P as hi + lo bf16 pairs; element e of the operand is token 16(e / 4) + 4grp + e % 4.
+    unsigned hi[4], lo[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float p0 = p[w >> 1][2 * (w & 1)], p1 = p[w >> 1][2 * (w & 1) + 1];
+      unsigned h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
+      hi[w] = (h0 >> 16) | h1;
+      lo[w] = pack_bf16(p0 - __uint_as_float(h0), p1 - __uint_as_float(h1));
+    }
+    bf16x8_t Ph = as_bf16x8(u32x4{hi[0], hi[1], hi[2], hi[3]});
+    bf16x8_t Pl = as_bf16x8(u32x4{lo[0], lo[1], lo[2], lo[3]});
+    if constexpr (KVT == 1) {
+#pragma unroll
+      for (int mt = 0; mt < GE::NMT; ++mt) {
+        bf16x8_t A = as_bf16x8(vr[mt]);
+        O[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Ph, O[mt], 0, 0, 0);
+        O[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pl, O[mt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < GE::NL; ++j) {
+        u32x2 b0 = fp8x4_to_bf16x4(vr[j].x), b1 = fp8x4_to_bf16x4(vr[j].y);
+        u32x2 b2 = fp8x4_to_bf16x4(vr[j].z), b3 = fp8x4_to_bf16x4(vr[j].w);
+        bf16x8_t A0 = as_bf16x8(u32x4{b0.x, b0.y, b1.x, b1.y});
+        bf16x8_t A1 = as_bf16x8(u32x4{b2.x, b2.y, b3.x, b3.y});
+        O[2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Ph, O[2 * j], 0, 0, 0);
+        O[2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Pl, O[2 * j], 0, 0, 0);
+        O[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Ph, O[2 * j + 1], 0, 0, 0);
+        O[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Pl, O[2 * j + 1], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int KVT, int D>
+__device__ __forceinline__ void load_page(const uint8_t* kb, PageRegs<KVT, D>& kr,
+                                          PageRegs<KVT, D>& vr, uint32_t block_bytes) {
+  using GE = Geo<KVT, D>;
+  const uint8_t* k = kb + 16 * lane_id();
+  const uint8_t* v = k + block_bytes;
+#pragma unroll
+  for (int j = 0; j < GE::NL; ++j) kr[j] = load16(k + 1024 * j);
+#pragma unroll
+  for (int j = 0; j < GE::NL; ++j) vr[j] = load16(v + 1024 * j);
+}
+
+// State of one work unit's online softmax.
+template <int KVT, int D>
+struct Acc {
+  ORegs<KVT, D> O;
+  float m;  // running max (base-2 scaled scores) of head n
+  float l;  // this lane's partial sum of weights
+};
+
+// Processes one page into the accumulators.
+template <int KVT, int D>
+__device__ __forceinline__ void page_step(const AttnParams& P, Acc<KVT, D>& A, const PageRegs<KVT, D>& kr,
+                                          PageRegs<KVT, D>& vr, const QRegs<KVT, D>& qv,
+                                          const QFRegs<KVT, D>& qf, int pg, int p_row) {
+  using GE = Geo<KVT, D>;
+  const int grp = lane_id() >> 4;
+  f32x4_t S[2];
+  page_scores<KVT, D>(kr, qv, qf, S);
+  bool valid[2][4];
+  float s[2][4];
+  float mx = -INFINITY;
+  const int t0 = pg * kPage + 4 * grp;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      valid[a][i] = t0 + 16 * a + i <= p_row;
+      s[a][i] = valid[a][i] ? S[a][i] * P.qk_scale : -INFINITY;
+      mx = fmaxf(mx, s[a][i]);
+    }
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  const float m_new = fmaxf(A.m, mx);
+  const float alpha = exp2f(A.m - m_new);
+  float p[2][4];
+  float ls = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[a][i] = exp2f(s[a][i] - m_new);
+      ls += p[a][i];
+    }
+  A.l = A.l * alpha + ls;
+  A.m = m_new;
+#pragma unroll
+  for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] *= alpha;
+  if ((pg + 1) * kPage > p_row + 1) mask_v<KVT, D>(vr, valid);  // partial last page
+  page_pv<KVT, D>(vr, p, A.O);
+}
+
+// Runs pages [pg0, pg1) of row r, kv head g.  Loads of the next page are issued
+// before the current page is reduced.
+template <int KVT, int D>
+__device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, int r, int s, int p_row, int g,
+                                         int pg0, int pg1) {
+  using GE = Geo<KVT, D>;
+  u32x4 qv[GE::NQ];
+  float qf[GE::NQ];
+  load_q<KVT, D>(P, r, g, qv, qf);
+#pragma unroll
+  for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  A.m = -INFINITY;
+  A.l = 0.f;
+  const int32_t* trow = P.table + (int64_t)s * P.max_pages;
+  const uint8_t* base = P.pages + (uint64_t)g * 2 * P.block_bytes;
+  u32x4 k0[GE::NL], v0[GE::NL], k1[GE::NL], v1[GE::NL];
+  load_page<KVT, D>(base + (uint64_t)trow[pg0] * P.page_stride, k0, v0, P.block_bytes);
+  int pg = pg0;
+  for (; pg + 1 < pg1; pg += 2) {
+    load_page<KVT, D>(base + (uint64_t)trow[pg + 1] * P.page_stride, k1, v1, P.block_bytes);
+    page_step<KVT, D>(P, A, k0, v0, qv, qf, pg, p_row);
+    if (pg + 2 < pg1) load_page<KVT, D>(base + (uint64_t)trow[pg + 2] * P.page_stride, k0, v0, P.block_bytes);
+    page_step<KVT, D>(P, A, k1, v1, qv, qf, pg + 1, p_row);
+  }
+  if (pg < pg1) page_step<KVT, D>(P, A, k0, v0, qv, qf, pg, p_row);
+}
+
+// Sum of the lane-partial l over the four 16-lane groups (fixed butterfly).
+__device__ __forceinline__ float group_sum(float l) {
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  return l;
+}
+
+template <int D>
+__device__ __forceinline__ void store_out4(const AttnParams& P, int r, int h, int c, f32x4_t v) {
+  if (P.out_bf16) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + c;
+    *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  } else {
+    float* o = reinterpret_cast<float*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + c;
+    *reinterpret_cast<f32x4_t*>(o) = v;
+  }
+}
+
+// Final normalisation and store of the G heads of kv head g.
+template <int KVT, int D>
+__device__ __forceinline__ void finish(const AttnParams& P, const Acc<KVT, D>& A, int r, int g) {
+  using GE = Geo<KVT, D>;
+  const int l = lane_id(), grp = l >> 4, n = l & 15;
+  const float lsum = group_sum(A.l);
+  if (n >= P.G) return;
+  const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int mt = 0; mt < GE::NMT; ++mt) {
+    f32x4_t v = A.O[mt] * inv * P.v_scale;
+    store_out4<D>(P, r, g * P.G + n, 16 * mt + 4 * grp, v);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void zero_heads(const AttnParams& P, int r, int g) {
+  const int l = lane_id(), grp = l >> 4, n = l & 15;
+  if (n >= P.G) return;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) store_out4<D>(P, r, g * P.G + n, 16 * mt + 4 * grp, f32x4_t{0.f, 0.f, 0.f, 0.f});
+}
+
+// One wave per (row, kv head); every row is a single chunk.
+template <int KVT, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_direct_kernel(AttnParams P) {
+  const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
+  const int s = P.seq[r], p = P.pos[r];
+  if (!row_ok(P, s, p, g == 0)) {
+    zero_heads<D>(P, r, g);
+    return;
+  }
+  Acc<KVT, D> A;
+  run_unit<KVT, D>(P, A, r, s, p, g, 0, (p + kPage) / kPage);
+  finish<KVT, D>(P, A, r, g);
+}
+
+// Chunked mode, step 1 (one workgroup of 1024 threads): chunk count of every
+// row, exclusive prefix sum, reset of the work counter.
+__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnParams P, int32_t* row_chunks) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x, n = P.n_rows;
+  const int per = (n + 1023) / 1024;
+  const int r0 = min(n, t * per), r1 = min(n, r0 + per);
+  int32_t sum = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int s = P.seq[r], p = P.pos[r];
+    unsigned e = 0;
+    if (s < 0 || s >= P.max_seqs) e = kErrSeq;
+    else if (p < 0 || p >= kPage * P.counts[s]) e = kErrPos;
+    int32_t c = 0;
+    if (e) atomicOr(P.err, e);
+    else c = ((p + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages;
+    row_chunks[r] = c;
+    sum += c;
+  }
+  part[t] = sum;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums
+  for (int off = 1; off < 1024; off <<= 1) {
+    int32_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int32_t run = part[t] - sum;
+  int32_t* cs = const_cast<int32_t*>(P.chunk_start);
+  for (int r = r0; r < r1; ++r) {
+    cs[r] = run;
+    run += row_chunks[r];
+  }
+  if (t == 1023) {
+    cs[n] = part[1023];
+    *const_cast<int32_t*>(P.total_units) = part[1023];
+    *P.counter = 0;
+  }
+}
+
+// Chunked mode, step 2: persistent waves take (row, chunk, kv head) units from a
+// counter.  A row with one chunk is finished here; others leave (m, l, O).
+template <int KVT, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunked_kernel(AttnParams P) {
+  using GE = Geo<KVT, D>;
+  const int total = *P.total_units * P.n_kv;
+  const int l = lane_id(), grp = l >> 4, n = l & 15;
+  for (;;) {
+    int item = 0;
+    if (l == 0) item = atomicAdd(P.counter, 1);
+    item = __shfl(item, 0, kWave);
+    if (item >= total) break;
+    const int u = item / P.n_kv, g = item % P.n_kv;
+    int lo = 0, hi = P.n_rows;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.chunk_start[mid] <= u) lo = mid; else hi = mid;
+    }
+    const int r = lo, c = u - P.chunk_start[r];
+    const int nch = P.chunk_start[r + 1] - P.chunk_start[r];
+    const int s = P.seq[r], p = P.pos[r];
+    const int npg = (p + kPage) / kPage;
+    const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
+    Acc<KVT, D> A;
+    run_unit<KVT, D>(P, A, r, s, p, g, pg0, pg1);
+    if (nch == 1) {
+      finish<KVT, D>(P, A, r, g);
+      continue;
+    }
+    const float lsum = group_sum(A.l);
+    if (n < P.G) {
+      const int64_t rec = ((int64_t)u * P.n_kv + g) * P.G + n;
+      if (grp == 0) {
+        P.part_ml[2 * rec] = A.m;
+        P.part_ml[2 * rec + 1] = lsum;
+      }
+#pragma unroll
+      for (int mt = 0; mt < GE::NMT; ++mt)
+        *reinterpret_cast<f32x4_t*>(P.part_o + rec * D + 16 * mt + 4 * grp) = A.O[mt];
+    }
+  }
+}
+
+// Chunked mode, step 3: one wave per (row, kv head) merges the chunk results
+// of rows with more than one chunk, in ascending chunk order; rows refused by
+// the plan get zeros.
+template <int D>
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
+  const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
+  const int c0 = P.chunk_start[r], nch = P.chunk_start[r + 1] - c0;
+  if (nch == 1) return;
+  const int l = lane_id();
+  constexpr int PER = D / 64;  // dims per lane
+  for (int n = 0; n < P.G; ++n) {
+    const int h = g * P.G + n;
+    float o[PER];
+    if (nch == 0) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) o[j] = 0.f;
+    } else {
+      float M = -INFINITY;
+      for (int c = 0; c < nch; ++c) M = fmaxf(M, P.part_ml[2 * (((int64_t)(c0 + c) * P.n_kv + g) * P.G + n)]);
+      float L = 0.f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) o[j] = 0.f;
+      for (int c = 0; c < nch; ++c) {
+        const int64_t rec = ((int64_t)(c0 + c) * P.n_kv + g) * P.G + n;
+        const float w = exp2f(P.part_ml[2 * rec] - M);
+        L += P.part_ml[2 * rec + 1] * w;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) o[j] += P.part_o[rec * D + PER * l + j] * w;
+      }
+      const float inv = 1.0f / L;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) o[j] = o[j] * inv * P.v_scale;
+    }
+    if (P.out_bf16) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + PER * l;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) dst[j] = (uint16_t)f32_to_bf16_bits(o[j]);
+    } else {
+      float* dst = reinterpret_cast<float*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + PER * l;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) dst[j] = o[j];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ append
+// Writes each row's own key and value at (seq, pos), converted to the pool
+// dtype, into the layout of include/pkd.h.  One wave per (row, kv head).
+template <int KVT, int D>
+__global__ __launch_bounds__(64) void append_kernel(AttnParams P, const void* k_new, const void* v_new,
+                                                    int64_t kv_stride, float inv_k, float inv_v, float k_scale,
+                                                    float v_scale) {
+  const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
+  const int s = P.seq[r], p = P.pos[r];
+  if (!row_ok(P, s, p, g == 0)) return;
+  const int page = P.table[(int64_t)s * P.max_pages + p / kPage];
+  const int t = p % kPage;
+  uint8_t* kb = const_cast<uint8_t*>(P.pages) + (uint64_t)page * P.page_stride + (uint64_t)g * 2 * P.block_bytes;
+  uint8_t* vb = kb + P.block_bytes;
+  const int l = lane_id();
+  const int64_t src = (int64_t)r * kv_stride + (int64_t)g * D;
+  (void)inv_k; (void)inv_v; (void)k_scale; (void)v_scale;
+  if constexpr (KVT == 0) {
+    const float* kn = reinterpret_cast<const float*>(k_new) + src;
+    const float* vn = reinterpret_cast<const float*>(v_new) + src;
+    float* K = reinterpret_cast<float*>(kb);
+    float* V = reinterpret_cast<float*>(vb);
+    for (int c = l; c < D; c += kWave) {
+      K[((t / 16) * (D / 4) + c / 4) * 64 + (t % 16) * 4 + c % 4] = kn[c];
+      const int a = t / 16, b = (t % 16) / 4, i = t % 4;
+      V[(((a * (D / 16) + c / 16) * 4 + b) * 16 + c % 16) * 4 + i] = vn[c];
+    }
+  } else if constexpr (KVT == 1) {
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(k_new) + src;
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(v_new) + src;
+    uint16_t* K = reinterpret_cast<uint16_t*>(kb);
+    uint16_t* V = reinterpret_cast<uint16_t*>(vb);
+    for (int c = l; c < D; c += kWave) {
+      K[((t / 16) * (D / 8) + c / 8) * 128 + (t % 16) * 8 + c % 8] = kn[c];
+      const int a = t / 16, b = (t % 16) / 4, i = t % 4;
+      V[(((c / 16) * 4 + b) * 16 + c % 16) * 8 + 4 * a + i] = vn[c];
+    }
+  } else {
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(k_new) + src;
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(v_new) + src;
+    for (int c = l; c < D; c += kWave) {
+      // value / scale in fp32 (true division), then E4M3 RNE with saturation
+      const float kq = bf16_bits_to_f32(kn[c]) / k_scale;
+      const float vq = bf16_bits_to_f32(vn[c]) / v_scale;
+      const unsigned codes = f32x2_to_fp8x2(kq, vq);
+      kb[((t / 16) * (D / 16) + c / 16) * 256 + (t % 16) * 16 + c % 16] = (uint8_t)(codes & 0xff);
+      const int a = t / 16, b = (t % 16) / 4, i = t % 4;
+      vb[(((c / 32) * 4 + b) * 16 + c % 16) * 16 + 8 * ((c / 16) % 2) + 4 * a + i] = (uint8_t)(codes >> 8);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host
+struct AttnWs {
+  int32_t* row_chunks;
+  int32_t* chunk_start;
+  int32_t* total;
+  int32_t* counter;
+  float* part_ml;
+  float* part_o;
+};
+
+static bool chunked(const pkd_pool* pool) {
+  return pool->desc.attn_chunk_pages < pool->desc.max_pages_per_seq;
+}
+
+static size_t max_units(const pkd_pool* pool, int32_t rows) {
+  const int64_t per = (pool->desc.max_pages_per_seq + pool->desc.attn_chunk_pages - 1) / pool->desc.attn_chunk_pages;
+  return (size_t)rows * (size_t)per;
+}
+
+static size_t carve(const pkd_pool* pool, int32_t n_q_heads, int32_t rows, uint8_t* base, AttnWs* w) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  if (!chunked(pool)) {
+    if (w) *w = AttnWs{};
+    return 0;
+  }
+  const int G = n_q_heads / pool->desc.num_kv_heads;
+  const size_t units = max_units(pool, rows) * pool->desc.num_kv_heads * G;
+  AttnWs t;
+  t.row_chunks = (int32_t*)take(sizeof(int32_t) * (rows + 1));
+  t.chunk_start = (int32_t*)take(sizeof(int32_t) * (rows + 1));
+  t.total = (int32_t*)take(sizeof(int32_t) * 4);
+  t.counter = (int32_t*)take(sizeof(int32_t) * 4);
+  t.part_ml = (float*)take(sizeof(float) * 2 * units);
+  t.part_o = (float*)take(sizeof(float) * (size_t)pool->desc.head_dim * units);
+  if (w) *w = t;
+  return off;
+}
+
+size_t attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t max_rows) {
+  if (!pool || max_rows < 0 || n_q_heads <= 0) return 0;
+  return carve(pool, n_q_heads, max_rows, nullptr, nullptr);
+}
+
+template <int KVT, int D>
+static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk,
+                       hipStream_t st) {
+  const int units = a.n_rows * n_kv;
+  if (a.k_new) {
+    const float ks = a.pool->desc.k_scale, vs = a.pool->desc.v_scale;
+    hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P, a.k_new, a.v_new, a.kv_new_stride,
+                       1.0f / ks, 1.0f / vs, ks, vs);
+  }
+  if (!chunk) {
+    hipLaunchKernelGGL((attn_direct_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
+    return;
+  }
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, st, P, w.row_chunks);
+  const int grid = 256 * 8;
+  hipLaunchKernelGGL((attn_chunked_kernel<KVT, D>), dim3(grid), dim3(64), 0, st, P);
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units), dim3(64), 0, st, P);
+}
+
+pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err) {
+  const pkd_pool* pool = a.pool;
+  const pkd_pool_desc& d = pool->desc;
+  if (a.n_rows == 0) return ok(err);
+  const size_t need = carve(pool, a.n_q_heads, a.n_rows, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)need, (int64_t)(ws ? ws_bytes : 0),
+                "attention workspace too small: need %zu bytes", need);
+  if (need > 0 && ((uintptr_t)ws & 255))
+    return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "workspace must be 256-byte aligned");
+  AttnWs w;
+  carve(pool, a.n_q_heads, a.n_rows, (uint8_t*)ws, &w);
+  AttnParams P{};
+  P.pages = pool->base + pool->info.pages_offset;
+  P.block_bytes = (uint32_t)pool->info.block_bytes;
+  P.page_stride = (uint64_t)d.num_kv_heads * 2 * pool->info.block_bytes;
+  P.table = (const int32_t*)(pool->base + pool->info.table_offset);
+  P.counts = (const int32_t*)(pool->base + pool->info.counts_offset);
+  P.max_pages = d.max_pages_per_seq;
+  P.max_seqs = d.max_seqs;
+  P.err = (uint32_t*)(pool->base + pool->info.error_offset);
+  P.seq = a.seq;
+  P.pos = a.pos;
+  P.n_rows = a.n_rows;
+  P.n_kv = d.num_kv_heads;
+  P.G = a.n_q_heads / d.num_kv_heads;
+  P.q = a.q;
+  P.q_stride = a.q_stride;
+  P.out = a.out;
+  P.out_bf16 = a.out_dtype == PKD_BF16;
+  P.out_stride = a.out_stride;
+  P.qk_scale = (float)(1.4426950408889634 / sqrt((double)d.head_dim)) * d.k_scale;
+  P.v_scale = d.v_scale;
+  P.chunk_pages = d.attn_chunk_pages;
+  P.chunk_start = w.chunk_start;
+  P.total_units = w.total;
+  P.counter = w.counter;
+  P.part_ml = w.part_ml;
+  P.part_o = w.part_o;
+  const bool ch = chunked(pool);
+  const int kvt = d.kv_dtype;
+  if (d.head_dim == 128) {
+    if (kvt == PKD_F32) launch_all<0, 128>(P, a, w, d.num_kv_heads, ch, stream);
+    else if (kvt == PKD_BF16) launch_all<1, 128>(P, a, w, d.num_kv_heads, ch, stream);
+    else launch_all<2, 128>(P, a, w, d.num_kv_heads, ch, stream);
+  } else {
+    if (kvt == PKD_F32) launch_all<0, 64>(P, a, w, d.num_kv_heads, ch, stream);
+    else if (kvt == PKD_BF16) launch_all<1, 64>(P, a, w, d.num_kv_heads, ch, stream);
+    else launch_all<2, 64>(P, a, w, d.num_kv_heads, ch, stream);
+  }
+  return check_launch(err, "paged attention");
+}
+
+}  // namespace pkd

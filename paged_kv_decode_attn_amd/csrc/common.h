@@ -1,0 +1,135 @@
+// Device and host helpers shared by the libpkd kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkd.h"
+
+namespace pkd {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+constexpr int kWave = 64;
+constexpr int kPage = 32;
+
+// ------------------------------------------------------------------ formats
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ unsigned f32_to_bf16_bits(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned b) { return __uint_as_float(b << 16); }
+// Two bf16 packed in one dword: low half element 0, high half element 1.
+__device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// Two E4M3 codes (bytes 0/1 of `w` when hi = false, bytes 2/3 when true) -> floats.
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(unsigned w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+// Four E4M3 codes -> two dwords of bf16 (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(unsigned w) {
+  f32x2_t a = fp8x2_to_f32(w, false), b = fp8x2_to_f32(w, true);
+  u32x2 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  return r;
+}
+// Clamps to the E4M3 range, keeping NaN (the hardware conversion does not saturate).
+__device__ __forceinline__ float sat448(float x) {
+  return (x != x) ? x : fminf(fmaxf(x, -448.0f), 448.0f);
+}
+// Two floats -> two E4M3 codes (RNE, saturating) in the low 16 bits.
+__device__ __forceinline__ unsigned f32x2_to_fp8x2(float a, float b) {
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false) & 0xffffu;
+}
+
+// ------------------------------------------------------------------ wave ops
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Butterfly sum over the 64 lanes: every lane ends with the same value, formed by
+// the same fixed tree for every call (pairs at distance 32, 16, ..., 1).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+// ------------------------------------------------------------------ sticky errors
+enum : unsigned { kErrSeq = 1u, kErrPos = 2u, kErrPage = 4u };
+
+}  // namespace pkd
+
+// ------------------------------------------------------------------ host side
+struct pkd_pool {
+  pkd_pool_desc desc;
+  uint8_t* base;
+  size_t bytes;
+  pkd_pool_info info;
+  int device;
+};
+
+namespace pkd {
+
+size_t align256(size_t x);
+pkd_status fail(pkd_error* err, pkd_status code, int64_t needed, int64_t available, const char* fmt, ...);
+pkd_status ok(pkd_error* err);
+pkd_status check_launch(pkd_error* err, const char* what);
+int elem_size(int dtype);
+
+// Attention launch used by paged_attn_decode and decode_step.
+struct AttnArgs {
+  const pkd_pool* pool;
+  const int32_t* seq;
+  const int32_t* pos;
+  int32_t n_rows;
+  int32_t n_q_heads;
+  const void* q;
+  int64_t q_stride;  // elements between rows
+  const void* k_new;
+  const void* v_new;
+  int64_t kv_new_stride;
+  void* out;
+  int32_t out_dtype;
+  int64_t out_stride;
+};
+size_t attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t max_rows);
+pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err);
+
+// Projection launch used by gemv_rows and decode_step.
+struct ProjArgs {
+  const pkd_matrix* W;
+  const void* x;
+  int32_t x_dtype;
+  int32_t n_rows;
+  void* y;
+  int32_t out_dtype;
+  const float* residual;
+  int32_t silu_pair;
+  void* y_bf16;
+};
+size_t proj_workspace_bytes(const pkd_matrix* W, int32_t max_rows);
+pkd_status proj_validate(const ProjArgs& a, pkd_error* err);
+pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err);
+
+// Elementwise f32 -> bf16 rounding of n values (projection inputs).
+pkd_status cast_bf16_launch(const float* x, void* y, int64_t n, hipStream_t stream, pkd_error* err);
+
+}  // namespace pkd

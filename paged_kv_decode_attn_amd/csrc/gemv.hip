@@ -1,0 +1,251 @@
+// Weight matrix-vector products for decode batches (vector ALU, fp32 accumulate).
+//
+// At decode batch sizes a projection reads every weight once per step, so its
+// speed is the speed at which the weight rows stream in from HBM ("llm-rs",
+// section 2); the small-matvec speed is set by how a row maps onto the lanes
+// and onto memory transactions (section 3), which the one-warp-per-output-row
+// kernel of section 4 addresses.  Here: one 64-lane wavefront owns NR weight
+// rows; lane l reads the 16-byte vectors l, l + 64, l + 128, ... of each row,
+// so every load instruction of the wave is one contiguous 1 KiB run.  The R
+// activation rows of the launch are held in registers per k-vector and each
+// weight is used R times from its register ("GPU inference engine
+// engineering", section "The same bits in any batch": register-tiled
+// projections).  Each output is a lane-sequential fp32 sum over its k-vectors
+// followed by a butterfly over the 64 lanes whose tree (pairs at distance 32,
+// 16, 8, 4, 2, 1) is the same for every R, so the result of an activation row
+// does not depend on how many rows share the launch.
+
+#include "common.h"
+
+namespace pkd {
+
+struct GemvParams {
+  const uint8_t* W;
+  int32_t rows;  // weight rows (outputs; 2F with silu)
+  int32_t cols;
+  float w_scale;
+  const uint8_t* x;
+  int64_t x_stride;  // elements
+  int32_t n_rows;
+  void* y;
+  int32_t y_bf16;
+  int64_t y_stride;  // elements
+  const float* residual;
+  uint16_t* y2;  // optional bf16 copy
+  int32_t n_out;  // outputs per activation row (rows, or rows / 2 with silu)
+};
+
+// Element count of one 16-byte weight vector.
+template <int WT>
+struct WV {
+  static constexpr int E = WT == 0 ? 4 : WT == 1 ? 8 : 16;
+};
+
+// Decodes one 16-byte weight vector into E floats.
+template <int WT>
+__device__ __forceinline__ void decode_w(u32x4 v, float* w) {
+  if constexpr (WT == 0) {
+    w[0] = __uint_as_float(v.x); w[1] = __uint_as_float(v.y);
+    w[2] = __uint_as_float(v.z); w[3] = __uint_as_float(v.w);
+  } else if constexpr (WT == 1) {
+    unsigned d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { w[2 * i] = bf16lo(d[i]); w[2 * i + 1] = bf16hi(d[i]); }
+  } else {
+    unsigned d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x2_t a = fp8x2_to_f32(d[i], false), b = fp8x2_to_f32(d[i], true);
+      w[4 * i] = a[0]; w[4 * i + 1] = a[1]; w[4 * i + 2] = b[0]; w[4 * i + 3] = b[1];
+    }
+  }
+}
+
+// Loads E activation values of row r at element k (f32 or bf16 storage).
+template <int XT, int E>
+__device__ __forceinline__ void load_x(const uint8_t* x, int64_t stride, int r, int k, float* out) {
+  if constexpr (XT == 0) {
+    const float* p = reinterpret_cast<const float*>(x) + (int64_t)r * stride + k;
+#pragma unroll
+    for (int i = 0; i < E; i += 4) {
+      f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + i);
+      out[i] = v[0]; out[i + 1] = v[1]; out[i + 2] = v[2]; out[i + 3] = v[3];
+    }
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + (int64_t)r * stride + k;
+#pragma unroll
+    for (int i = 0; i < E; i += 8) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(p + i);
+      unsigned d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { out[i + 2 * j] = bf16lo(d[j]); out[i + 2 * j + 1] = bf16hi(d[j]); }
+    }
+  }
+}
+
+// Reduces v[0..R) over the 64 lanes; afterwards the lanes whose bits 5..(6 -
+// log2 R) spell row j hold that row's total (all four lanes of a group of 4
+// when R = 16).  Returns the row this lane holds.
+template <int C, int M, int R>
+__device__ __forceinline__ void transpose_step(float (&v)[R], int l, int& row) {
+  if constexpr (C > 1) {
+    const bool b = (l & M) != 0;
+#pragma unroll
+    for (int j = 0; j < C / 2; ++j) {
+      const float send = b ? v[j] : v[C / 2 + j];
+      const float recv = shfl_xor(send, M);
+      v[j] = (b ? v[C / 2 + j] : v[j]) + recv;
+    }
+    row = 2 * row + (b ? 1 : 0);
+    transpose_step<C / 2, M / 2, R>(v, l, row);
+  } else {
+#pragma unroll
+    for (int m = M; m >= 1; m >>= 1) v[0] += shfl_xor(v[0], m);
+  }
+}
+
+template <int R>
+__device__ __forceinline__ int transpose_reduce(float (&v)[R]) {
+  int row = 0;
+  transpose_step<R, 32, R>(v, lane_id(), row);
+  return row;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// NR weight rows per wave (SILU: NR / 2 gate rows j and the matching up rows
+// F + j), R activation rows per launch tile (blockIdx.y), 4 waves per block.
+template <int WT, int XT, int R, int NR, bool SILU>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
+  constexpr int E = WV<WT>::E;
+  constexpr int NP = SILU ? NR / 2 : NR;  // outputs per wave
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = lane_id();
+  const int o0 = wave * NP;  // first output of this wave
+  if (o0 >= P.n_out) return;
+  const int r0 = blockIdx.y * R;
+  const int F = P.n_out;
+  int wrow[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    int o = SILU ? (i < NP ? o0 + i : F + o0 + (i - NP)) : o0 + i;
+    const int last = SILU ? (i < NP ? F - 1 : 2 * F - 1) : P.rows - 1;
+    wrow[i] = min(o, last);  // rows past the end repeat the last row; not stored
+  }
+  const int64_t row_bytes = (int64_t)P.cols * (WT == 0 ? 4 : WT == 1 ? 2 : 1);
+  const int nvec = P.cols / E;
+  float acc[NR][R];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
+  constexpr int U = 4;  // k-vectors per lane in flight per row
+  for (int j0 = l; j0 < nvec; j0 += 64 * U) {
+    u32x4 wv[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 64 * u;
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        wv[u][i] = j < nvec ? *reinterpret_cast<const u32x4*>(P.W + wrow[i] * row_bytes + 16 * (int64_t)j)
+                            : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 64 * u;
+      if (j >= nvec) break;
+      float w[NR][E];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) decode_w<WT>(wv[u][i], w[i]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r0 + r >= P.n_rows) break;  // uniform: rows past the batch keep zero sums
+        float xv[E];
+        load_x<XT, E>(P.x, P.x_stride, r0 + r, E * j, xv);
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[i][r] = fmaf(w[i][e], xv[e], acc[i][r]);
+      }
+    }
+  }
+  int row = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    row = transpose_reduce<R>(acc[i]);
+    acc[i][0] *= P.w_scale;
+  }
+  // one writer lane per activation row: the lane whose low bits are zero
+  constexpr int LOG_R = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : R == 8 ? 3 : 4;
+  const bool writer = (l & ((64 >> LOG_R) - 1)) == 0;
+  const int r = r0 + row;
+  if (!writer || r >= P.n_rows) return;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int o = o0 + i;
+    if (o >= P.n_out) break;
+    float v;
+    if constexpr (SILU) {
+      v = silu(acc[i][0]) * acc[NP + i][0];
+    } else {
+      v = acc[i][0];
+      if (P.residual) v += P.residual[(int64_t)r * P.n_out + o];
+    }
+    if (P.y_bf16) reinterpret_cast<uint16_t*>(P.y)[(int64_t)r * P.y_stride + o] = (uint16_t)f32_to_bf16_bits(v);
+    else reinterpret_cast<float*>(P.y)[(int64_t)r * P.y_stride + o] = v;
+    if (P.y2) P.y2[(int64_t)r * P.n_out + o] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+template <int WT, int XT, int R, bool SILU>
+static void launch_r(const GemvParams& P, hipStream_t st) {
+  constexpr int NR = 4;
+  constexpr int NP = SILU ? NR / 2 : NR;
+  const int waves = (P.n_out + NP - 1) / NP;
+  dim3 grid((waves + 3) / 4, (P.n_rows + R - 1) / R);
+  hipLaunchKernelGGL((gemv_kernel<WT, XT, R, NR, SILU>), grid, dim3(256), 0, st, P);
+}
+
+template <int WT, int XT, bool SILU>
+static void launch_x(const GemvParams& P, hipStream_t st) {
+  const int n = P.n_rows;
+  if (n <= 1) launch_r<WT, XT, 1, SILU>(P, st);
+  else if (n <= 2) launch_r<WT, XT, 2, SILU>(P, st);
+  else if (n <= 4) launch_r<WT, XT, 4, SILU>(P, st);
+  else if (n <= 8) launch_r<WT, XT, 8, SILU>(P, st);
+  else launch_r<WT, XT, 16, SILU>(P, st);
+}
+
+template <int WT>
+static void launch_w(const GemvParams& P, int xt, bool silu, hipStream_t st) {
+  if (xt == PKD_F32) {
+    if (silu) launch_x<WT, 0, true>(P, st); else launch_x<WT, 0, false>(P, st);
+  } else {
+    if (silu) launch_x<WT, 1, true>(P, st); else launch_x<WT, 1, false>(P, st);
+  }
+}
+
+pkd_status gemv_launch(const ProjArgs& a, hipStream_t stream, pkd_error* err) {
+  const pkd_matrix& W = *a.W;
+  GemvParams P{};
+  P.W = (const uint8_t*)W.data;
+  P.rows = W.rows;
+  P.cols = W.cols;
+  P.w_scale = W.scale;
+  P.x = (const uint8_t*)a.x;
+  P.x_stride = W.cols;
+  P.n_rows = a.n_rows;
+  P.y = a.y;
+  P.y_bf16 = a.out_dtype == PKD_BF16;
+  P.n_out = a.silu_pair ? W.rows / 2 : W.rows;
+  P.y_stride = P.n_out;
+  P.residual = a.residual;
+  P.y2 = (uint16_t*)a.y_bf16;
+  const bool silu = a.silu_pair != 0;
+  if (W.dtype == PKD_F32) launch_w<0>(P, a.x_dtype, silu, stream);
+  else if (W.dtype == PKD_BF16) launch_w<1>(P, a.x_dtype, silu, stream);
+  else launch_w<2>(P, a.x_dtype, silu, stream);
+  return check_launch(err, "gemv_rows");
+}
+
+}  // namespace pkd

@@ -1,0 +1,195 @@
+"""Parity of the HIP paged attention (with and without the append of the row's
+own token) against the fp64 oracle, element by element; bit-identity across
+batch compositions and runs; invalid rows; chunked and unchunked reduction."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+# Tolerances: the kernel reads the same stored codes as the oracle and reduces
+# in fp32 (scores by the matrix core, weights as a hi + lo bf16 pair with ~16
+# significant bits), so the attention output agrees to ~1e-5 relative;
+# 1e-4 leaves a margin of ~10x.  Outputs stored in bf16 add one rounding of
+# at most 2^-8 relative.
+TOL_F32_OUT = 1e-4
+TOL_BF16_OUT = 2 ** -8 + 1e-4
+
+
+@pytest.fixture(scope="module")
+def H():
+    import gpu_harness
+    return gpu_harness
+
+
+def oracle_attn(orc, w, seq, pos, q, k_new=None, v_new=None):
+    hk, hv = wl.history_lists(w)
+    hist = orc.History(hk, hv, w.kv_dtype, w.n_kv, w.head_dim)
+    qd = w.q_dtype
+    tonp = lambda t: None if t is None else wl.to_numpy_codes(t, qd)
+    return orc.attention(w.n_q, w.n_kv, w.head_dim, w.kv_dtype, w.k_scale, w.v_scale, hist, seq, pos, qd,
+                         tonp(q), tonp(k_new), tonp(v_new))
+
+
+CASES = [
+    # (kv dtype, n_q, n_kv, d, append, chunk)
+    (wl.F32, 4, 2, 64, True, 2),
+    (wl.F32, 4, 2, 64, False, 8),
+    (wl.BF16, 4, 2, 128, True, 2),
+    (wl.BF16, 4, 2, 128, False, 8),
+    (wl.BF16, 14, 2, 128, True, 1),
+    (wl.BF16, 2, 2, 128, True, 3),
+    (wl.BF16, 32, 2, 64, True, 2),
+    (wl.FP8, 14, 2, 128, True, 2),
+    (wl.FP8, 4, 2, 64, False, 8),
+    (wl.BF16, 7, 1, 128, True, 8),
+]
+
+
+@pytest.mark.parametrize("kvt,nq,nkv,d,append,chunk", CASES)
+def test_attention_parity(H, orc, kvt, nq, nkv, d, append, chunk):
+    lens = (1, 2, 31, 32, 33, 63, 64, 65, 97, 160, 200)
+    w = wl.make("attn", "cpu", seed=11 + nq + d + kvt, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens,
+                append=append, chunk=chunk)
+    print(f"case {w.name} append={append} chunk={chunk}", flush=True)
+    pool = H.GpuPool(w)
+    dev = lambda t: None if t is None else t.to("cuda")
+    out = H.run_attention(pool, w.seq, w.pos, dev(w.q), dev(w.k_new), dev(w.v_new), wl.F32)
+    want = oracle_attn(orc, w, w.seq, w.pos, w.q, w.k_new, w.v_new)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    e = H.rel_err(got, want)
+    print(f"  max rel err {e:.3e}")
+    assert e <= TOL_F32_OUT
+    # L = 1 (first row): the output is the value of token 0 (bit-exact outside fp8)
+    if kvt != wl.FP8:
+        assert np.array_equal(got[0], want[0])
+    # bf16 output = RNE of the f32 output
+    if kvt != wl.F32:
+        if append:  # re-run from a fresh pool: the append must not be applied twice differently
+            pool = H.GpuPool(w)
+        ob = H.run_attention(pool, w.seq, w.pos, dev(w.q), dev(w.k_new), dev(w.v_new), wl.BF16)
+        gb = H.values(ob, wl.BF16)
+        assert H.rel_err(gb, want) <= TOL_BF16_OUT
+        assert np.array_equal(gb, torch.from_numpy(got).float().to(torch.bfloat16).double().numpy())
+
+
+def test_attention_batch_invariance(H):
+    """A row gives the same bits alone, in the full batch, in a shuffled batch,
+    in a subset, and on a repeated run; chunked and direct pools each."""
+    for chunk in (2, 8):
+        lens = (5, 33, 64, 65, 150, 199, 200, 256)
+        w = wl.make("attn", "cpu", seed=3, n_q=14, n_kv=2, d=128, kv_dtype=wl.BF16, lens=lens, append=False,
+                    chunk=chunk)
+        pool = H.GpuPool(w)
+        q = w.q.to("cuda")
+        full = H.run_attention(pool, w.seq, w.pos, q).cpu()
+        again = H.run_attention(pool, w.seq, w.pos, q).cpu()
+        assert torch.equal(full, again)
+        perm = np.asarray([6, 2, 7, 0, 5, 1, 4, 3])
+        sh = H.run_attention(pool, w.seq[perm], w.pos[perm], q[torch.as_tensor(perm, device="cuda")]).cpu()
+        assert torch.equal(sh, full[torch.as_tensor(perm)])
+        for r in (0, 4, 7):
+            one = H.run_attention(pool, w.seq[r:r + 1], w.pos[r:r + 1], q[r:r + 1]).cpu()
+            assert torch.equal(one[0], full[r])
+        # the same row repeated many times in one batch
+        reps = np.full(300, 6, np.int32)
+        many = H.run_attention(pool, w.seq[reps], w.pos[reps], q[6:7].expand(300, -1, -1).contiguous()).cpu()
+        assert torch.equal(many, full[6:7].expand(300, -1, -1))
+
+
+def test_attention_rows_of_one_sequence(H, orc):
+    """Several rows of one sequence in one call (a prefill slice): all appends
+    land before any read, so row p sees the tokens of rows < p."""
+    w = wl.make("attn", "cpu", seed=5, n_q=4, n_kv=2, d=128, kv_dtype=wl.BF16, lens=(40,), append=True,
+                chunk=2, extra_pages=3)
+    # rows at positions 39..70 of sequence 0, with fresh k/v for each
+    gen = torch.Generator().manual_seed(9)
+    n = 32
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(39, 39 + n, dtype=np.int32)
+    q = wl.encode(torch.randn((n, 4, 128), generator=gen), wl.BF16)
+    kn = wl.encode(torch.randn((n, 2, 128), generator=gen), wl.BF16)
+    vn = wl.encode(torch.randn((n, 2, 128), generator=gen), wl.BF16)
+    pool = H.GpuPool(w)
+    out = H.run_attention(pool, seq, pos, q.cuda(), kn.cuda(), vn.cuda())
+    want = oracle_attn(orc, w, seq, pos, q, kn, vn)
+    assert H.rel_err(out.cpu().numpy(), want) <= TOL_F32_OUT
+    # the pool now holds the appended tokens: read them back through the oracle's gather
+    pages = pool.pages_bytes().cpu().numpy()
+    k, v = orc.gather_history(pages, 2, 128, wl.BF16, w.tables[0], 39 + n)
+    assert np.array_equal(k[39:].view(np.uint16), wl.to_numpy_codes(kn, wl.BF16))
+    assert np.array_equal(v[39:].view(np.uint16), wl.to_numpy_codes(vn, wl.BF16))
+
+
+def test_fp8_append_codes(H, orc):
+    """The appended fp8 codes are E4M3 RNE(value / scale) with saturation,
+    exactly as the oracle encodes them (values beyond the calibrated range
+    included)."""
+    w = wl.make("attn", "cpu", seed=6, n_q=4, n_kv=2, d=128, kv_dtype=wl.FP8, lens=(10, 45), append=True,
+                chunk=2)
+    gen = torch.Generator().manual_seed(1)
+    kn = wl.encode(torch.randn((2, 2, 128), generator=gen) * 3.0, wl.BF16)  # some past 448 * scale
+    vn = wl.encode(torch.randn((2, 2, 128), generator=gen) * 3.0, wl.BF16)
+    pool = H.GpuPool(w)
+    H.run_attention(pool, w.seq, w.pos, w.q.cuda(), kn.cuda(), vn.cuda())
+    pages = pool.pages_bytes().cpu().numpy()
+    for s in range(2):
+        L = int(w.pos[s]) + 1
+        k, v = orc.gather_history(pages, 2, 128, wl.FP8, w.tables[s], L)
+        kv = orc.bf16_value(wl.to_numpy_codes(kn[s], wl.BF16))
+        vv = orc.bf16_value(wl.to_numpy_codes(vn[s], wl.BF16))
+        want_k = orc.e4m3_round((kv.astype(np.float32) / np.float32(w.k_scale)).astype(np.float64))
+        want_v = orc.e4m3_round((vv.astype(np.float32) / np.float32(w.v_scale)).astype(np.float64))
+        assert np.array_equal(k[L - 1], want_k)
+        assert np.array_equal(v[L - 1], want_v)
+        assert (k[L - 1] == 0x7E).any() or (k[L - 1] == 0xFE).any()  # saturation exercised
+
+
+def test_invalid_rows_zeroed_and_reported(H):
+    import paged_kv_decode_attn_amd as pkd
+    for chunk in (1, 8):  # chunked and direct reduction
+        w = wl.make("attn", "cpu", seed=7, n_q=4, n_kv=2, d=128, kv_dtype=wl.BF16, lens=(20, 40), append=False,
+                    chunk=chunk, extra_pages=0)
+        pool = H.GpuPool(w)
+        seq = np.asarray([0, 5, 1, 1, -1], np.int32)
+        pos = np.asarray([19, 3, 64, 39, 0], np.int32)  # seq 5 absent, pos 64 past 2 pages, seq -1
+        q = torch.cat([w.q] * 3)[:5].cuda()
+        out = H.run_attention(pool, seq, pos, q).cpu()
+        assert torch.equal(out[1], torch.zeros_like(out[1]))
+        assert torch.equal(out[2], torch.zeros_like(out[2]))
+        assert torch.equal(out[4], torch.zeros_like(out[4]))
+        assert out[0].abs().sum() > 0 and out[3].abs().sum() > 0
+        with pytest.raises(pkd.PkdError) as ei:
+            pkd.pkd_pool_check(pool.handle)
+        assert ei.value.status == 7 and ei.value.needed == 3  # bad sequence and bad position
+        pkd.pkd_pool_check(pool.handle)  # cleared
+
+
+def test_block_table_refusals(H):
+    import paged_kv_decode_attn_amd as pkd
+    w = wl.make("attn", "cpu", seed=8, n_q=4, n_kv=2, d=64, kv_dtype=wl.F32, lens=(20, 40), append=False,
+                chunk=2)
+    pool = H.GpuPool(w)
+    mp = w.max_pages_per_seq
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.block_table_set(pool.handle, 0, np.zeros((1, mp), np.int32), [mp + 1])
+    assert ei.value.status == 4 and ei.value.needed == mp + 1 and ei.value.available == mp
+    bad = np.zeros((1, mp), np.int32)
+    bad[0, 0] = w.num_pages
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.block_table_set(pool.handle, 0, bad, [1])
+    assert ei.value.status == 4 and ei.value.needed == w.num_pages and ei.value.available == w.num_pages
+    dup = np.zeros((1, mp), np.int32)
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.block_table_set(pool.handle, 0, dup, [2])
+    assert ei.value.status == 5
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.block_table_set(pool.handle, 1, w.tables, w.counts)
+    assert ei.value.status == 4 and ei.value.needed == 3 and ei.value.available == 2
+    # refused calls changed nothing: attention still matches a fresh pool
+    out = H.run_attention(pool, w.seq, w.pos, w.q.cuda()).cpu()
+    fresh = H.run_attention(H.GpuPool(w), w.seq, w.pos, w.q.cuda()).cpu()
+    assert torch.equal(out, fresh)

@@ -351,7 +351,48 @@ def _b4096_fp8(gen, rng, dev, n: int = 4096, L: int = 1024, family: int = MFMA,
                     k_scale=ks, v_scale=vs)
 
 
+def _attn_case(gen, rng, dev, n_q=4, n_kv=2, d=128, kv_dtype=BF16, lens=(1, 31, 32, 33, 64, 65, 100),
+               append=True, chunk=2, extra_pages=3, shared_first_page=False):
+    """Attention-only case: one row per sequence at position len - 1; the pool
+    holds len - 1 positions (append) or all len positions; pages at random,
+    `extra_pages` spare pages per sequence reserved in the tables."""
+    lens = np.asarray(lens, np.int32)
+    S = len(lens)
+    need = (lens + 31) // 32
+    reserve = need + extra_pages
+    num_pages = int(reserve.sum()) + 3
+    perm = rng.permutation(num_pages)
+    lists, o = [], 0
+    for n in reserve:
+        lists.append(perm[o:o + n].tolist()); o += n
+    if shared_first_page and S > 1:
+        for s in range(1, S):
+            if lens[s] > 32 and lens[0] >= 32:
+                lists[s][0] = lists[0][0]
+    max_pages = int(reserve.max())
+    tables, counts = _finish_tables(lists, S, max_pages)
+    hist_len = (lens - 1 if append else lens).astype(np.int32)
+    hk, hv, ks, vs = _history(gen, dev, int(hist_len.sum()), n_kv, d, kv_dtype)
+    off = _offsets(hist_len)
+    if shared_first_page:
+        for s in range(1, S):
+            if lens[s] > 32 and lens[0] >= 32:
+                hk[off[s]:off[s] + 32] = hk[off[0]:off[0] + 32]
+                hv[off[s]:off[s] + 32] = hv[off[0]:off[0] + 32]
+    qd = F32 if kv_dtype == F32 else BF16
+    x = torch.zeros((S, 64), device=dev)
+    w = Workload(f"attn-{['f32', 'bf16', 'fp8'][kv_dtype]}-g{n_q // n_kv}-d{d}", 64, n_q, n_kv, d, 0, qd,
+                 kv_dtype, qd, GEMV, 0, chunk, num_pages, S, max_pages, tables, counts, hist_len, off, hk, hv,
+                 np.arange(S, dtype=np.int32), (lens - 1).astype(np.int32), x, k_scale=ks, v_scale=vs)
+    w.q = encode(torch.randn((S, n_q, d), generator=gen, device=dev), qd)
+    if append:
+        w.k_new = encode(torch.randn((S, n_kv, d), generator=gen, device=dev), qd)
+        w.v_new = encode(torch.randn((S, n_kv, d), generator=gen, device=dev), qd)
+    return w
+
+
 BUILDERS = {
+    "attn": _attn_case,
     "tiny-f32": _tiny,
     "0.6b-b1-bf16": _b1_06,
     "0.6b-mixed-bf16": _mixed_06,
