@@ -263,12 +263,17 @@ pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_h
  */
 typedef struct {
   const void* data;
-  int32_t rows;   /* outputs */
-  int32_t cols;   /* inputs, multiple of 64 */
-  int32_t dtype;  /* pkd_dtype */
-  float scale;    /* fp8: per-tensor scale (code x scale = weight); 1 otherwise */
-  int32_t family; /* pkd_family, fixed per matrix so a row's result never
-                     depends on how many rows share the launch */
+  int32_t rows;     /* outputs */
+  int32_t cols;     /* inputs, multiple of 64 */
+  int32_t dtype;    /* pkd_dtype */
+  float scale;      /* fp8: per-tensor scale (code x scale = weight); 1 otherwise */
+  int32_t family;   /* pkd_family, fixed per matrix so a row's result never
+                       depends on how many rows share the launch */
+  int32_t k_splits; /* matrix-core families: 0 or 1 = one pass over K; S > 1 =
+                       K cut into S fixed ranges whose fp32 partial sums are
+                       added in ascending order (more workgroups for matrices
+                       with few output tiles).  Fixed per matrix, like the
+                       family, so results stay batch invariant. */
 } pkd_matrix;
 
 /*

@@ -57,7 +57,8 @@ class pkd_rows(ctypes.Structure):
 
 class pkd_matrix(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("family", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("family", ctypes.c_int32),
+                ("k_splits", ctypes.c_int32)]
 
 
 class pkd_epilogue(ctypes.Structure):
@@ -196,8 +197,8 @@ def paged_attn_decode(pool, rows: pkd_rows, n_q_heads: int, q, k_new, v_new, out
 
 # ------------------------------------------------------------------ projections
 def make_matrix(data: torch.Tensor, rows: int, cols: int, dtype: int, scale: float = 1.0,
-                family: int = FAMILY_GEMV) -> pkd_matrix:
-    return pkd_matrix(_ptr(data), rows, cols, dtype, scale, family)
+                family: int = FAMILY_GEMV, k_splits: int = 1) -> pkd_matrix:
+    return pkd_matrix(_ptr(data), rows, cols, dtype, scale, family, k_splits)
 
 
 def pkd_gemv_workspace_bytes(W: pkd_matrix, max_rows: int) -> int:

@@ -141,6 +141,9 @@ pkd_status proj_validate(const ProjArgs& a, pkd_error* err) {
                   "matrix-core family needs rows %% 128 == 0 and cols %% %d == 0 (got %d x %d)", kb, W->rows, W->cols);
     if (W->dtype == PKD_BF16 && a.x_dtype != PKD_BF16)
       return fail(err, PKD_ERR_UNSUPPORTED, a.x_dtype, PKD_BF16, "bf16 matrix-core family needs bf16 activations");
+    if (W->k_splits < 0 || W->k_splits > W->cols / kb)
+      return fail(err, PKD_ERR_UNSUPPORTED, W->k_splits, W->cols / kb, "k_splits %d outside 0..%d for %d columns",
+                  W->k_splits, W->cols / kb, W->cols);
   }
   return PKD_OK;
 }
