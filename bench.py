@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b-b768-prefix-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--family", type=int, default=None, help="override the projection family")
     return ap.parse_args()
 
@@ -93,7 +93,7 @@ def main():
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
     w = wl.make(args.workload, "cuda", **kw)
     pool = H.GpuPool(w)
-    layer = H.GpuLayer(w)
+    layer = H.GpuLayer(w, batch_hint=w.n_rows)  # engine built for this batch: fixed K splits
     L = layer.layer
     B, D, nq, nkv, d, F = w.n_rows, w.hidden, w.n_q, w.n_kv, w.head_dim, w.ffn
     stream = torch.cuda.current_stream()

@@ -297,6 +297,18 @@ typedef struct {
 size_t pkd_gemv_workspace_bytes(const pkd_matrix* W, int32_t max_rows);
 
 /*
+ * A k_splits value for a matrix-core matrix of rows x cols that will mostly
+ * see batches of about typical_rows rows: the S in {1, 2, 3, 4, 6, 8}, with
+ * at least 1536 columns per split, that minimises the estimated time at that
+ * batch (rounds of workgroups over the compute units times the K-work of one
+ * workgroup; a larger S must win by 5%).  The caller fixes
+ * the result in the pkd_matrix once (results depend on S, never on the batch
+ * it later runs).  Returns 1 for the GEMV family or invalid sizes.  Pure host
+ * function: no device access.
+ */
+int32_t pkd_suggest_k_splits(int32_t rows, int32_t cols, int32_t family, int32_t typical_rows);
+
+/*
  * y = epilogue(W x_r) for each of the n_rows rows of x (device [n_rows][cols]).
  *   GEMV family: x is f32 or bf16 and is used exactly; fp32 accumulation.
  *   MFMA family, bf16 weights: x must be bf16; fp32 accumulation.

@@ -75,7 +75,7 @@ class pkd_layer(ctypes.Structure):
 
 EXPORTS = ["pkd_pool_bytes", "kv_pool_create", "kv_pool_destroy", "pkd_pool_info_get", "block_table_set",
            "pkd_pool_check", "pkd_attn_workspace_bytes", "paged_attn_decode", "pkd_gemv_workspace_bytes",
-           "gemv_rows", "pkd_step_workspace_bytes", "decode_step", "pkd_status_string", "pkd_version"]
+           "pkd_suggest_k_splits", "gemv_rows", "pkd_step_workspace_bytes", "decode_step", "pkd_status_string", "pkd_version"]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -95,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkd_attn_workspace_bytes": (SZ, [P, I32, I32]),
         "paged_attn_decode": (I32, [P, ctypes.POINTER(pkd_rows), I32, P, P, P, P, I32, P, SZ, P, E]),
         "pkd_gemv_workspace_bytes": (SZ, [ctypes.POINTER(pkd_matrix), I32]),
+        "pkd_suggest_k_splits": (I32, [I32, I32, I32, I32]),
         "gemv_rows": (I32, [ctypes.POINTER(pkd_matrix), P, I32, I32, P, ctypes.POINTER(pkd_epilogue), P, SZ,
                             P, E]),
         "pkd_step_workspace_bytes": (SZ, [ctypes.POINTER(pkd_layer), P, I32]),
@@ -203,6 +204,10 @@ def make_matrix(data: torch.Tensor, rows: int, cols: int, dtype: int, scale: flo
 
 def pkd_gemv_workspace_bytes(W: pkd_matrix, max_rows: int) -> int:
     return lib().pkd_gemv_workspace_bytes(ctypes.byref(W), max_rows)
+
+
+def pkd_suggest_k_splits(rows: int, cols: int, family: int, typical_rows: int) -> int:
+    return lib().pkd_suggest_k_splits(rows, cols, family, typical_rows)
 
 
 def gemv_rows(W: pkd_matrix, x, x_dtype: int, n_rows: int, y, out_dtype: int = F32, residual=None,

@@ -335,6 +335,10 @@ pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_h
 
 size_t pkd_gemv_workspace_bytes(const pkd_matrix* W, int32_t max_rows) { return proj_workspace_bytes(W, max_rows); }
 
+int32_t pkd_suggest_k_splits(int32_t rows, int32_t cols, int32_t family, int32_t typical_rows) {
+  return suggest_k_splits(rows, cols, family, typical_rows);
+}
+
 pkd_status gemv_rows(const pkd_matrix* W, const void* x, int32_t x_dtype, int32_t n_rows, void* y,
                      const pkd_epilogue* ep, void* ws, size_t ws_bytes, pkd_stream stream, pkd_error* err) {
   if (!ep) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "epilogue is NULL");

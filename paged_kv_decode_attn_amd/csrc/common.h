@@ -126,6 +126,7 @@ struct ProjArgs {
   void* y_bf16;
 };
 size_t proj_workspace_bytes(const pkd_matrix* W, int32_t max_rows);
+int suggest_k_splits(int rows, int cols, int family, int typical_rows);
 pkd_status proj_validate(const ProjArgs& a, pkd_error* err);
 pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err);
 

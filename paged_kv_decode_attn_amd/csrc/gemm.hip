@@ -8,15 +8,16 @@
 // contracts fp8 weights with per-row fp8 activations ("Engines for the card you
 // have", section "One checkpoint, many engines").
 //
-// Workgroup tile: 256 weight rows x 128 activation rows, eight waves of
-// 64 x 64 (4 x 4 matrix-core tiles of 16 x 16; two waves per SIMD so that one
-// wave's LDS and memory waits overlap the other's products), k-tile of 128
-// bytes per row.
-// LDS holds [256 weight rows; 128 activation rows] x 128 bytes per stage with
-// an XOR swizzle of the 16-byte chunks (row r, chunk c at c ^ (r & 7)), so the
-// operand reads of a wave hit distinct banks.
-//   mode 0 (bf16) and mode 2 (native fp8): three stages fed by direct
-//     global-to-LDS loads (global_load_lds_dwordx4), waited on explicitly;
+// Workgroup tile: TN = 256 weight rows x TM = 128 or 256 activation rows, k-tile
+// of 128 bytes per row, eight waves (two per SIMD, so that one wave's LDS and
+// memory waits overlap the other's products).  TM = 256: waves of 128 x 64
+// (8 x 4 matrix-core tiles of 16 x 16), two LDS stages of 64 KiB; TM = 128:
+// waves of 64 x 64, three stages of 48 KiB.  The taller tile halves the bytes
+// each CU pulls from L2 per product; the shorter one keeps small batches busy.
+// LDS rows hold 128 bytes with an XOR swizzle of the 16-byte chunks (row r,
+// chunk c at c ^ (r & 7)), so the operand reads of a wave hit distinct banks.
+//   mode 0 (bf16) and mode 2 (native fp8): stages fed by buffer loads that
+//     write LDS directly (buffer_load_dwordx4 ... lds), waited on explicitly;
 //   mode 1 (fp8 decoded to bf16): the codes pass through registers, are widened
 //     exactly to bf16 and stored; two stages.
 // The k-loop order is fixed; a row's outputs never depend on which rows share
@@ -50,24 +51,44 @@ struct GemmParams {
   float* partial;  // splits > 1: [splits][M][N] raw fp32 sums
 };
 
-constexpr int TN = 256, TM = 128, TKB = 128;   // tile rows, k-tile bytes per LDS row
-constexpr int ROWS = TN + TM;                  // LDS rows per stage
-constexpr int STAGE_BYTES = ROWS * TKB;        // 48 KiB
+constexpr int TN = 256;  // weight rows per tile
 constexpr int NWAVES = 8;
-constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / NWAVES;  // 6 wave loads of 1 KiB each
+template <int MODE, int TM>
+struct Tile {
+  // LDS bytes per row and stage: two 32-wide bf16 k-steps (modes 0, 1; mode 1
+  // widened from fp8), one 128-wide fp8 k-step (mode 2)
+  static constexpr int KB = 128;
+  static constexpr int STAGE_BYTES = (TN + TM) * KB;
+  static constexpr int STAGES = MODE == 1 ? 2 : (TM == 256 ? 2 : 3);
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;            // at most 144 KiB
+  static constexpr int DPW = STAGE_BYTES / 1024 / NWAVES;            // 1 KiB wave loads per stage
+  static constexpr int RPB = 1024 / KB;                              // LDS rows per 1 KiB block
+  static constexpr int MW = TM / 64;                                 // waves along the activation rows
+  static constexpr int WN = TN / (NWAVES / MW);                      // weight rows per wave: 128 or 64
+  static constexpr int WA = WN / 16;                                 // weight tiles per wave
+};
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 #define PKD_VMCNT(n) (0x0F70 | ((n) & 0xF) | (((n) & 0x30) << 10))
 
-// One 16-byte-per-lane load from global memory straight into LDS: lane l's
-// 16 bytes land at lds + 16 l (lds is wave-uniform).  The host compilation
-// pass never sees the device builtin.
-__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds) {
+// Raw buffer view of an operand: loads past num_records bytes (checked per
+// dword, SGPR offset included) return zeros instead of touching memory, which
+// is how tiles that overhang the last weight or activation row are filled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_view(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte-per-lane load from an operand view straight into LDS: lane l's
+// 16 bytes (at voff + soff) land at lds + 16 l (lds is wave-uniform).  The
+// host compilation pass never sees the device builtin.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, (int)soff, 0, 0);
 #else
-  (void)g;
+  (void)r;
+  (void)voff;
+  (void)soff;
   (void)lds;
 #endif
 }
@@ -79,195 +100,249 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * TKB + ((chunk ^ (row & 7)) << 4); }
-
-// Global weight row of LDS tile row rho (< TN).  silu: each 64-row quarter of
-// the tile (one wave's rows) is 32 gate rows followed by the 32 matching up rows.
-__device__ __forceinline__ int w_row(const GemmParams& P, int n0, int rho) {
-  if (!P.silu) return min(n0 + rho, P.N - 1);
-  const int F = P.N / 2, j0 = n0 / 2, wn = rho >> 6, q = rho & 63;
-  const int j = min(j0 + 32 * wn + (q & 31), F - 1);
-  return q < 32 ? j : F + j;
+// Byte offset of 16-byte chunk `chunk` of LDS row `row` (rows of KB bytes).
+// The XOR spreads the 16 rows that one matrix-core operand read touches over
+// all 64 banks: 128-byte rows use row & 7, 64-byte rows (four per 256 bytes)
+// use (row >> 2) & 3.
+template <int KB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (KB == 128) return row * 128 + ((chunk ^ (row & 7)) << 4);
+  else return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
+// Global weight row of LDS tile row rho (< TN).  silu: each wave's slab of WN
+// rows is WN / 2 gate rows followed by the WN / 2 matching up rows.
+template <int WN>
+__device__ __forceinline__ int w_row(const GemmParams& P, int n0, int rho) {
+  if (!P.silu) return min(n0 + rho, P.N - 1);
+  const int F = P.N / 2, j0 = n0 / 2, wn = rho / WN, q = rho % WN;
+  const int j = min(j0 + (WN / 2) * wn + q % (WN / 2), F - 1);
+  return q < WN / 2 ? j : F + j;
+}
+
+template <int WN, int TM>
 __device__ __forceinline__ const uint8_t* row_ptr(const GemmParams& P, int n0, int m0, int rho, int64_t kbytes) {
-  if (rho < TN) return P.W + (int64_t)w_row(P, n0, rho) * kbytes;
+  if (rho < TN) return P.W + (int64_t)w_row<WN>(P, n0, rho) * kbytes;
   return P.X + (int64_t)min(m0 + rho - TN, P.M - 1) * kbytes;
 }
 
-template <int MODE>
+template <int MODE, int TM>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
+  using T = Tile<MODE, TM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr bool NATIVE8 = MODE == 2;
-  constexpr int STAGES = MODE == 1 ? 2 : 3;
+  constexpr int STAGES = T::STAGES, KB = T::KB, RPB = T::RPB;
+  constexpr int SB = T::STAGE_BYTES, DPW = T::DPW, WN = T::WN, WA = T::WA;
   // work item -> (tile n, split, tile m), dealt contiguously per XCD
   const int items = P.tiles_n * P.splits * P.tiles_m;
   const int b = blockIdx.x;
-  const int item = (items % 8 == 0) ? (b % 8) * (items / 8) + b / 8 : b;
+  // blocks go to the 8 XCDs round-robin (XCD b % 8); XCD x takes the
+  // contiguous items [x base + min(x, rem), ...), one extra for x < rem
+  const int base8 = items / 8, rem8 = items % 8, xcd = b % 8;
+  const int item = xcd * base8 + min(xcd, rem8) + b / 8;
   const int tm = item % P.tiles_m;
   const int sp = (item / P.tiles_m) % P.splits;
   const int tn = item / (P.tiles_m * P.splits);
   const int n0 = tn * TN, m0 = tm * TM;
   const int t = threadIdx.x, wave = t >> 6, l = t & 63, grp = l >> 4, i16 = l & 15;
-  const int wn = wave >> 1, wm = wave & 1;  // wn 0..3 (64 weight rows), wm 0..1 (64 activation rows)
+  const int wn = wave / T::MW, wm = wave % T::MW;  // weight slab of WN rows, activation slab of 64 rows
   const int64_t kbytes = MODE == 0 ? 2 * (int64_t)P.K : P.K;  // HBM bytes per operand row
-  const int nk_all = MODE == 2 ? P.K / 128 : P.K / 64;       // k-tiles over the whole K
+  constexpr int KT_BYTES = MODE == 1 ? 64 : KB;             // HBM bytes per row per k-tile
+  const int nk_all = (int)(kbytes / KT_BYTES);               // k-tiles over the whole K
   const int kt0 = (int)((int64_t)nk_all * sp / P.splits), kt1 = (int)((int64_t)nk_all * (sp + 1) / P.splits);
   const int nk = kt1 - kt0;
-  constexpr int KT_BYTES = MODE == 1 ? 64 : TKB;  // HBM bytes per row per k-tile
 
   // ---- loaders
-  // DMA (modes 0, 2): wave w loads 1 KiB blocks 6w .. 6w + 5 of the stage;
-  // lane l lands at block + 16 l = row 8 * block + l / 8, swizzled chunk l % 8,
-  // so it reads global chunk (l % 8) ^ (l / 8) of that row.
-  const uint8_t* dsrc[MODE == 1 ? 1 : DMA_PER_WAVE];
-  // register path (mode 1): thread t moves fp8 chunks q = t + 512 j (j < 3),
-  // row q / 4, 16-byte chunk q % 4 of the 64-byte k-tile.
-  constexpr int NR = 3;
-  const uint8_t* rsrc[MODE == 1 ? NR : 1];
-  if constexpr (MODE != 1) {
+  // LDS buffer loads (modes 0, 2): wave w fills 1 KiB blocks b = DPW w + i of
+  // the stage, block b being LDS rows RPB b .. RPB b + RPB - 1; lane l lands
+  // at block + 16 l = row RPB b + l / CPR, swizzled chunk l % CPR, so it reads
+  // the global chunk that the swizzle puts there.  The lane part of the
+  // address is one VGPR; the block's first global row and the k offset are
+  // wave-uniform.
+  constexpr int CPR = KB / 16;  // 16-byte chunks per LDS row
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int lrow = l / CPR, lch = l % CPR;
+  const int gch = KB == 128 ? (lch ^ (lrow & 7)) : (lch ^ ((lrow >> 2) & 3));
+  const uint32_t voff = (uint32_t)(lrow * kbytes + 16 * gch);
+  const __amdgpu_buffer_rsrc_t wview = operand_view(P.W, (uint32_t)(P.N * kbytes));
+  const __amdgpu_buffer_rsrc_t xview = operand_view(P.X, (uint32_t)(P.M * kbytes));
+  // first global row of LDS block b (weight rows below TN, then activation rows)
+  auto block_row = [&](int b) -> int {
+    const int rho0 = RPB * b;
+    if (rho0 >= TN) return m0 + rho0 - TN;
+    if (!P.silu) return n0 + rho0;
+    const int slab = rho0 / WN, q0 = rho0 % WN;
+    const int j = n0 / 2 + (WN / 2) * slab + q0 % (WN / 2);
+    return q0 < WN / 2 ? j : P.N / 2 + j;
+  };
+  auto dma_issue = [&](int kt) {  // stage kt (local index) into buffer kt % STAGES
+    uint8_t* base = smem + (kt % STAGES) * SB + DPW * 1024 * wave_u;
+    const uint32_t koff = (uint32_t)(kt0 + kt) * KT_BYTES;
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int rho = 8 * (DMA_PER_WAVE * wave + i) + (l >> 3);
-      const int c = (l & 7) ^ (l >> 3);
-      dsrc[i] = row_ptr(P, n0, m0, rho, kbytes) + (int64_t)kt0 * KT_BYTES + 16 * c;
+    for (int i = 0; i < DPW; ++i) {
+      const int b = DPW * wave_u + i;
+      const uint32_t soff = (uint32_t)block_row(b) * (uint32_t)kbytes + koff;
+      lds_load16(RPB * b < TN ? wview : xview, voff, soff, base + 1024 * i);
     }
-  } else {
+  };
+  // register path (mode 1): thread t moves fp8 chunks q = t + 512 j (j < NR),
+  // row q / 4, 16-byte chunk q % 4 of the 64-byte k-tile.
+  constexpr int NR = (TN + TM) / 128;
+  const uint8_t* rsrc[MODE == 1 ? NR : 1];
+  if constexpr (MODE == 1) {
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       const int q = t + 512 * j;
-      rsrc[j] = row_ptr(P, n0, m0, q >> 2, kbytes) + (int64_t)kt0 * KT_BYTES + 16 * (q & 3);
+      rsrc[j] = row_ptr<WN, TM>(P, n0, m0, q >> 2, kbytes) + (int64_t)kt0 * KT_BYTES + 16 * (q & 3);
     }
   }
-  auto dma_issue = [&](int kt) {  // stage kt (local index) into buffer kt % STAGES
-    uint8_t* base = smem + (kt % STAGES) * STAGE_BYTES + DMA_PER_WAVE * 1024 * wave;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      lds_dma16(dsrc[i] + (int64_t)kt * KT_BYTES, base + 1024 * i);
-  };
   u32x4 rr[NR];
   auto reg_load = [&](int kt) {
 #pragma unroll
     for (int j = 0; j < NR; ++j) rr[j] = *reinterpret_cast<const u32x4*>(rsrc[j] + (int64_t)kt * KT_BYTES);
   };
   auto reg_store = [&](int buf) {
-    uint8_t* s = smem + buf * STAGE_BYTES;
+    uint8_t* s = smem + buf * SB;
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       const int q = t + 512 * j, rho = q >> 2, c = q & 3;
       const u32x2 a0 = fp8x4_to_bf16x4(rr[j].x), a1 = fp8x4_to_bf16x4(rr[j].y);
       const u32x2 a2 = fp8x4_to_bf16x4(rr[j].z), a3 = fp8x4_to_bf16x4(rr[j].w);
-      *reinterpret_cast<u32x4*>(s + swz(rho, 2 * c)) = u32x4{a0.x, a0.y, a1.x, a1.y};
-      *reinterpret_cast<u32x4*>(s + swz(rho, 2 * c + 1)) = u32x4{a2.x, a2.y, a3.x, a3.y};
+      *reinterpret_cast<u32x4*>(s + swz<KB>(rho, 2 * c)) = u32x4{a0.x, a0.y, a1.x, a1.y};
+      *reinterpret_cast<u32x4*>(s + swz<KB>(rho, 2 * c + 1)) = u32x4{a2.x, a2.y, a3.x, a3.y};
     }
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[WA][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < WA; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Operands of one k-tile in two halves.  bf16: half h = k-step h (4 weight
-  // and 4 activation tiles).  Native fp8 (one 128-wide k-step): half 0 = the 4
-  // activation tiles and weight tiles 0..1, half 1 = weight tiles 2..3.
-  // Registers: ob[h][0..3] weight operands, ob[h][4..7] activation operands.
-  u32x4 ob[2][8];
-  u32x4 oc[2][8];  // second dword-quad of each native fp8 operand (32 bytes per lane)
-  auto read_half = [&](const uint8_t* s, int h) {
+  // bf16 operands of k-step h (of two 32-wide steps per stage): the wave's WA
+  // weight tiles and 4 activation tiles, row i16 of each 16-row tile, 16 bytes
+  // at k-chunk 4 h + grp.
+  auto read_ops = [&](const uint8_t* s, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) {
     const uint8_t* w = s;
-    const uint8_t* x = s + TN * TKB;
+    const uint8_t* x = s + TN * KB;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xo[c] = *reinterpret_cast<const u32x4*>(x + swz<KB>(wm * 64 + 16 * c + i16, 4 * h + grp));
+#pragma unroll
+    for (int a = 0; a < WA; ++a) wo[a] = *reinterpret_cast<const u32x4*>(w + swz<KB>(wn * WN + 16 * a + i16, 4 * h + grp));
+  };
+  auto mma = [&](const u32x4(&wo)[WA], const u32x4(&xo)[4]) {
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wo[a]),
+                                                            __builtin_bit_cast(bf16x8_t, xo[c]), acc[a][c], 0, 0, 0);
+  };
+  // Products of one whole LDS stage (the fp8 paths).  Native fp8: one k-step of
+  // 128, 32 bytes per lane (k-chunks 2 grp, 2 grp + 1), weight operands taken
+  // in two halves to bound the live registers.
+  auto compute = [&](const uint8_t* s) {
+    const uint8_t* w = s;
+    const uint8_t* x = s + TN * KB;
     if constexpr (!NATIVE8) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) ob[h][a] = *reinterpret_cast<const u32x4*>(w + swz(wn * 64 + 16 * a + i16, 4 * h + grp));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ob[h][4 + c] = *reinterpret_cast<const u32x4*>(x + swz(wm * 64 + 16 * c + i16, 4 * h + grp));
+      for (int h = 0; h < 2; ++h) {
+        u32x4 wo[WA], xo[4];
+        read_ops(s, h, wo, xo);
+        mma(wo, xo);
+      }
     } else {
-      if (h == 0) {
+      i32x8_t xo[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int row = wm * 64 + 16 * c + i16;
-          ob[0][4 + c] = *reinterpret_cast<const u32x4*>(x + swz(row, 2 * grp));
-          oc[0][4 + c] = *reinterpret_cast<const u32x4*>(x + swz(row, 2 * grp + 1));
-        }
-      } else {
-        // half 1 keeps its own copy of the tile's activation operands: the
-        // next tile's half-0 reads overwrite ob[0] before half 1 runs
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          ob[1][4 + c] = ob[0][4 + c];
-          oc[1][4 + c] = oc[0][4 + c];
-        }
+      for (int c = 0; c < 4; ++c) {
+        const int row = wm * 64 + 16 * c + i16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(x + swz<KB>(row, 2 * grp));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(x + swz<KB>(row, 2 * grp + 1));
+        xo[c] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int row = wn * 64 + 16 * (2 * h + a) + i16;
-        ob[h][a] = *reinterpret_cast<const u32x4*>(w + swz(row, 2 * grp));
-        oc[h][a] = *reinterpret_cast<const u32x4*>(w + swz(row, 2 * grp + 1));
+      for (int h = 0; h < 2; ++h) {
+        i32x8_t wo[WA / 2];
+#pragma unroll
+        for (int a = 0; a < WA / 2; ++a) {
+          const int row = wn * WN + 16 * (h * WA / 2 + a) + i16;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(w + swz<KB>(row, 2 * grp));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(w + swz<KB>(row, 2 * grp + 1));
+          wo[a] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int a = 0; a < WA / 2; ++a)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[h * WA / 2 + a][c] =
+                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wo[a], xo[c], acc[h * WA / 2 + a][c], 0, 0, 0, 127, 0, 127);
       }
     }
   };
-  auto mfma_half = [&](int h) {
-    if constexpr (!NATIVE8) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ob[h][a]),
-                                                              __builtin_bit_cast(bf16x8_t, ob[h][4 + c]), acc[a][c], 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 wl = ob[h][a], wh = oc[h][a], xl = ob[h][4 + c], xh = oc[h][4 + c];
-          const i32x8_t wo = {(int)wl.x, (int)wl.y, (int)wl.z, (int)wl.w, (int)wh.x, (int)wh.y, (int)wh.z, (int)wh.w};
-          const i32x8_t xo = {(int)xl.x, (int)xl.y, (int)xl.z, (int)xl.w, (int)xh.x, (int)xh.y, (int)xh.z, (int)xh.w};
-          acc[2 * h + a][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wo, xo, acc[2 * h + a][c], 0, 0, 0, 127, 0, 127);
-        }
+
+  // wait until at most n later stages' loads of this wave are outstanding
+  auto wait_stages = [&](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(PKD_VMCNT(DPW)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(PKD_VMCNT(2 * DPW)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(PKD_VMCNT(3 * DPW)); break;
+      default: __builtin_amdgcn_s_waitcnt(PKD_VMCNT(4 * DPW)); break;
     }
   };
 
-  // mode 1 keeps a single-phase compute over the LDS stage
-  auto compute_simple = [&](const uint8_t* s) {
-    read_half(s, 0);
-    read_half(s, 1);
-    mfma_half(0);
-    mfma_half(1);
-  };
-
-  if constexpr (MODE != 1) {
+  if constexpr (MODE == 0) {
+    // Ping-pong over the KS = KB / 64 k-steps of each stage: the operands of
+    // step g + 1 are read into one register set while the products of step g
+    // run on the other, so the matrix core does not wait on LDS.  At a stage
+    // boundary, once stage kt + 1 has landed everywhere (one barrier, which
+    // also retires every wave's reads of stage kt), stage kt's buffer is
+    // refilled with stage kt + STAGES.
+    constexpr int KS = KB / 64;
+    static_assert(STAGES - 2 <= 4, "wait_stages covers at most four later stages");
+    u32x4 w0[WA], x0[4], w1[WA], x1[4];
     const int pre = nk < STAGES ? nk : STAGES;
     for (int kt = 0; kt < pre; ++kt) dma_issue(kt);
-    // stage 0 landed: at most the loads of stages 1 .. pre - 1 remain
-    if (pre == 3) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(2 * DMA_PER_WAVE));
-    else if (pre == 2) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(DMA_PER_WAVE));
-    else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+    wait_stages(pre - 1);
     lds_barrier();
-    if (nk > 0) read_half(smem, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint8_t* cur = smem + (kt % STAGES) * STAGE_BYTES;
-      const uint8_t* nxt = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
-      // [A] second-half reads of tile kt under the first-half products
-      read_half(cur, 1);
-      mfma_half(0);
-      // [B] this wave's reads of tile kt are done and tile kt + 1 has landed
-      wait_lds_reads();
-      if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(DMA_PER_WAVE));
-      else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
-      lds_barrier();
-      // [C] refill the buffer of tile kt with tile kt + 3
-      if (kt + 3 < nk) dma_issue(kt + 3);
-      // [D] first-half reads of tile kt + 1 under the second-half products of tile kt
-      read_half(nxt, 0);
-      mfma_half(1);
-      // keep the prefetched operands in registers across the loop edge (the
-      // compiler would otherwise re-read them after the next barrier)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        asm volatile("" : "+v"(ob[0][i]));
-        if constexpr (NATIVE8) asm volatile("" : "+v"(oc[0][i]));
+    if (nk > 0) read_ops(smem, 0, w0, x0);
+    const int steps = nk * KS;
+    auto step = [&](int g, u32x4(&wc)[WA], u32x4(&xc)[4], u32x4(&wn_)[WA], u32x4(&xn)[4]) {
+      const int kt = g / KS, h = g % KS;
+      if (h + 1 < KS) {
+        read_ops(smem + (kt % STAGES) * SB, h + 1, wn_, xn);
+      } else if (kt + 1 < nk) {
+        const int later = nk - 2 - kt;
+        wait_stages(later < STAGES - 2 ? later : STAGES - 2);
+        wait_lds_reads();
+        lds_barrier();
+        if (kt + STAGES < nk) dma_issue(kt + STAGES);
+        read_ops(smem + ((kt + 1) % STAGES) * SB, 0, wn_, xn);
       }
+      mma(wc, xc);
+#pragma unroll
+      for (int a = 0; a < WA; ++a) asm volatile("" : "+v"(wn_[a]));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(xn[c]));
+    };
+    for (int g = 0; g < steps; g += 2) {
+      step(g, w0, x0, w1, x1);
+      if (g + 1 < steps) step(g + 1, w1, x1, w0, x0);
+    }
+  } else if constexpr (MODE == 2) {
+    // Stages kt .. kt + STAGES - 2 are in flight when tile kt's products start;
+    // one barrier per k-tile both publishes tile kt and retires every wave's
+    // reads of the buffer that the next load overwrites.
+    const int pre = nk < STAGES - 1 ? nk : STAGES - 1;
+    for (int kt = 0; kt < pre; ++kt) dma_issue(kt);
+    for (int kt = 0; kt < nk; ++kt) {
+      // this wave's loads of tile kt are done; later tiles may still be in flight
+      if (STAGES == 3 && kt + 1 < nk) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(DPW));
+      else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+      wait_lds_reads();
+      lds_barrier();
+      if (kt + STAGES - 1 < nk) dma_issue(kt + STAGES - 1);
+      compute(smem + (kt % STAGES) * SB);
     }
   } else {
     if (nk > 0) {
@@ -277,30 +352,32 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       if (kt + 1 < nk) reg_load(kt + 1);
-      compute_simple(smem + (kt & 1) * STAGE_BYTES);
+      compute(smem + (kt & 1) * SB);
       if (kt + 1 < nk) reg_store((kt + 1) & 1);
       __syncthreads();
     }
   }
 
-  // ---- epilogue: lane holds outputs n = n0 + wn*64 + 16a + 4grp + i of activation row
-  // m = m0 + wm*64 + 16c + i16
+  // ---- epilogue: lane holds outputs n = n0 + wn WN + 16a + 4grp + i of
+  // activation row m = m0 + wm 64 + 16c + i16.  silu: weight tiles a < WA / 2
+  // are gate rows j = n0 / 2 + wn WN / 2 + 16a + 4grp + i, tile a + WA / 2 the
+  // matching up rows.
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int m = m0 + wm * 64 + 16 * c + i16;
     if (m >= P.M) continue;
     if (P.splits > 1) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < WA; ++a) {
         if (!P.silu) {
-          const int n = n0 + wn * 64 + 16 * a + 4 * grp;
+          const int n = n0 + wn * WN + 16 * a + 4 * grp;
           if (n < P.N) *reinterpret_cast<f32x4_t*>(P.partial + ((int64_t)sp * P.M + m) * P.N + n) = acc[a][c];
         } else {
           // raw gate / up sums at their weight rows j and F + j
           const int F = P.N / 2;
-          const int j = n0 / 2 + wn * 32 + 16 * (a & 1) + 4 * grp;
+          const int j = n0 / 2 + wn * (WN / 2) + 16 * (a % (WA / 2)) + 4 * grp;
           if (j < F) {
-            const int nn = a < 2 ? j : F + j;
+            const int nn = a < WA / 2 ? j : F + j;
             *reinterpret_cast<f32x4_t*>(P.partial + ((int64_t)sp * P.M + m) * P.N + nn) = acc[a][c];
           }
         }
@@ -310,8 +387,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     const float rs = MODE != 0 ? P.x_scale[m] * P.w_scale : P.w_scale;
     if (!P.silu) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int n = n0 + wn * 64 + 16 * a + 4 * grp;
+      for (int a = 0; a < WA; ++a) {
+        const int n = n0 + wn * WN + 16 * a + 4 * grp;
         if (n >= P.N) continue;
         f32x4_t v = acc[a][c] * rs;
         if (P.residual) v += *reinterpret_cast<const f32x4_t*>(P.residual + (int64_t)m * P.n_out + n);
@@ -326,10 +403,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       }
     } else {
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int j = n0 / 2 + wn * 32 + 16 * a + 4 * grp;
+      for (int a = 0; a < WA / 2; ++a) {
+        const int j = n0 / 2 + wn * (WN / 2) + 16 * a + 4 * grp;
         if (j >= P.n_out) continue;
-        const f32x4_t g = acc[a][c] * rs, u = acc[a + 2][c] * rs;
+        const f32x4_t g = acc[a][c] * rs, u = acc[a + WA / 2][c] * rs;
         f32x4_t v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = g[i] / (1.0f + __expf(-g[i])) * u[i];
@@ -418,7 +495,46 @@ size_t proj_workspace_bytes(const pkd_matrix* W, int32_t max_rows) {
 
 pkd_status gemv_launch(const ProjArgs& a, hipStream_t stream, pkd_error* err);
 
-static bool lds_ready = false;
+template <int MODE, int TM>
+static void launch_tile(const GemmParams& P, int grid, hipStream_t stream) {
+  constexpr int lds = Tile<MODE, TM>::LDS_BYTES;
+  static bool attr = false;  // dynamic LDS above 64 KiB must be enabled once per kernel
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)gemm_kernel<MODE, TM>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((gemm_kernel<MODE, TM>), dim3(grid), dim3(64 * NWAVES), lds, stream, P);
+}
+
+// Activation tile height: 256 when that still gives every CU a tile, else 128.
+// Either height runs the same k-loop per output, so the choice never changes a
+// result.
+static int tile_m_for(int tiles_n, int splits, int M) {
+  const int items256 = tiles_n * splits * ((M + 255) / 256);
+  return items256 >= 256 ? 256 : 128;
+}
+
+
+// Estimated cost of a split: rounds of workgroups over the 256 CUs times the
+// work of one workgroup (tile height x its share of K).  A larger S must beat
+// the best so far by 5% to be taken (the partial sums cost a second pass).
+int suggest_k_splits(int rows, int cols, int family, int typical_rows) {
+  if (family == PKD_FAMILY_GEMV || rows <= 0 || cols <= 0 || typical_rows <= 0) return 1;
+  const int tiles_n = (rows + TN - 1) / TN;
+  int best = 1;
+  double best_cost = 0;
+  for (int s : {1, 2, 3, 4, 6, 8}) {
+    if (s > 1 && cols / s < 1536) break;
+    const int tm = tile_m_for(tiles_n, s, typical_rows);
+    const long items = (long)tiles_n * s * ((typical_rows + tm - 1) / tm);
+    const double cost = (double)((items + 255) / 256) * (tm / 128) * ((cols + s - 1) / s);
+    if (s == 1 || cost < 0.95 * best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err) {
   const pkd_matrix& W = *a.W;
@@ -429,6 +545,14 @@ pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t
     return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)need, (int64_t)(ws ? ws_bytes : 0),
                 "projection workspace too small: need %zu bytes", need);
   if (need && ((uintptr_t)ws & 255)) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "workspace must be 256-byte aligned");
+  {
+    // the tile loader addresses each operand with 32-bit byte offsets
+    const int64_t row_bytes = W.dtype == PKD_BF16 ? 2 * (int64_t)W.cols : (int64_t)W.cols;
+    if ((int64_t)(W.rows + 256) * row_bytes >= ((int64_t)1 << 31) ||
+        (int64_t)(a.n_rows + 256) * row_bytes >= ((int64_t)1 << 31))
+      return fail(err, PKD_ERR_UNSUPPORTED, (int64_t)W.rows, (int64_t)a.n_rows,
+                  "matrix-core projection operands must each be below 2 GiB");
+  }
   GemmParams P{};
   P.W = (const uint8_t*)W.data;
   P.w_scale = W.scale;
@@ -443,8 +567,9 @@ pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t
   P.residual = a.residual;
   P.y2 = (uint16_t*)a.y_bf16;
   P.tiles_n = (W.rows + TN - 1) / TN;
-  P.tiles_m = (a.n_rows + TM - 1) / TM;
   P.splits = splits_of(a.W);
+  const int tile_m = tile_m_for(P.tiles_n, P.splits, a.n_rows);
+  P.tiles_m = (a.n_rows + tile_m - 1) / tile_m;
   const bool fp8 = W.dtype == PKD_FP8_E4M3;
   const int mode = !fp8 ? 0 : (W.family == PKD_FAMILY_MFMA_FP8 ? 2 : 1);
   uint8_t* wsp = (uint8_t*)ws;
@@ -462,16 +587,16 @@ pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t
     P.X = (const uint8_t*)a.x;
   }
   P.partial = P.splits > 1 ? (float*)wsp : nullptr;
-  if (!lds_ready) {
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 3 * STAGE_BYTES);
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE_BYTES);
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 3 * STAGE_BYTES);
-    lds_ready = true;
-  }
   const int grid = P.tiles_n * P.splits * P.tiles_m;
-  if (mode == 0) hipLaunchKernelGGL(gemm_kernel<0>, dim3(grid), dim3(64 * NWAVES), 3 * STAGE_BYTES, stream, P);
-  else if (mode == 1) hipLaunchKernelGGL(gemm_kernel<1>, dim3(grid), dim3(64 * NWAVES), 2 * STAGE_BYTES, stream, P);
-  else hipLaunchKernelGGL(gemm_kernel<2>, dim3(grid), dim3(64 * NWAVES), 3 * STAGE_BYTES, stream, P);
+  if (tile_m == 256) {
+    if (mode == 0) launch_tile<0, 256>(P, grid, stream);
+    else if (mode == 1) launch_tile<1, 256>(P, grid, stream);
+    else launch_tile<2, 256>(P, grid, stream);
+  } else {
+    if (mode == 0) launch_tile<0, 128>(P, grid, stream);
+    else if (mode == 1) launch_tile<1, 128>(P, grid, stream);
+    else launch_tile<2, 128>(P, grid, stream);
+  }
   if (P.splits > 1) {
     const int64_t groups = (int64_t)P.M * (P.n_out / 4);
     const unsigned blocks = (unsigned)((groups + 255) / 256);

@@ -91,7 +91,11 @@ def run_attention(pool: GpuPool, seq, pos, q: torch.Tensor, k_new=None, v_new=No
 
 
 class GpuLayer:
-    def __init__(self, w: wl.Workload, family: int | None = None):
+    """Device copy of a workload's layer.  batch_hint: the batch the engine is
+    built for; matrix-core matrices then take the library's suggested K split
+    (fixed for the life of the layer, so results stay batch invariant)."""
+
+    def __init__(self, w: wl.Workload, family: int | None = None, batch_hint: int | None = None):
         self.w = w
         fam = w.family if family is None else family
         self.tensors = {k: v.to(DEV).contiguous() for k, v in w.weights.items()}
@@ -101,7 +105,8 @@ class GpuLayer:
         def M(name, rows, cols):
             if name not in self.tensors:
                 return pkd.pkd_matrix()
-            return pkd.make_matrix(self.tensors[name], rows, cols, w.w_dtype, w.scales.get(name, 1.0), fam)
+            S = pkd.pkd_suggest_k_splits(rows, cols, fam, batch_hint) if batch_hint else 1
+            return pkd.make_matrix(self.tensors[name], rows, cols, w.w_dtype, w.scales.get(name, 1.0), fam, S)
         self.layer = pkd.pkd_layer(D, nq, nkv, d, F, M("w_qkv", nqkv, D), M("w_o", D, nq * d),
                                    M("w_gu", 2 * F, D), M("w_d", D, F), w.act_dtype)
 

@@ -125,3 +125,20 @@ def test_null_handles_refused(pkd):
                                  ctypes.byref(err)) == 1
     assert pkd.lib().block_table_set(None, 0, 1, None, None, None, ctypes.byref(err)) == 1
     assert pkd.lib().pkd_pool_check(None, None, ctypes.byref(err)) == 1
+
+
+def test_suggested_k_splits(pkd):
+    """Host-only split policy: long-K and narrow matrices are split, a wide one
+    that already fills the chip is not, the vector family never is."""
+    D, F, M = 3584, 18944, 768
+    assert pkd.pkd_suggest_k_splits(4608, D, 1, M) == 2
+    assert pkd.pkd_suggest_k_splits(D, D, 1, M) == 2
+    assert pkd.pkd_suggest_k_splits(2 * F, D, 1, M) == 1
+    assert pkd.pkd_suggest_k_splits(D, F, 1, M) >= 3
+    assert pkd.pkd_suggest_k_splits(D, F, 0, M) == 1
+    assert pkd.pkd_suggest_k_splits(D, 1024, 1, M) == 1
+    assert pkd.pkd_suggest_k_splits(0, D, 1, M) == 1
+    for rows, cols in [(4608, D), (D, F), (2 * F, D)]:
+        for m in (1, 64, 768, 4096):
+            S = pkd.pkd_suggest_k_splits(rows, cols, 2, m)
+            assert S in (1, 2, 3, 4, 6, 8) and (S == 1 or cols // S >= 1536)

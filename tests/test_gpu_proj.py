@@ -56,10 +56,11 @@ def oracle_proj(orc, W, wdt, s, x, xdt, family, silu=False, residual=None):
     return y
 
 
-def run_proj(H, W, rows, cols, wdt, s, family, x, xdt, n, out_dtype, silu=False, residual=None, y2=False):
+def run_proj(H, W, rows, cols, wdt, s, family, x, xdt, n, out_dtype, silu=False, residual=None, y2=False,
+             k_splits=1):
     import paged_kv_decode_attn_amd as pkd
     Wd = W.cuda()
-    M = pkd.make_matrix(Wd, rows, cols, wdt, s, family)
+    M = pkd.make_matrix(Wd, rows, cols, wdt, s, family, k_splits)
     nout = rows // 2 if silu else rows
     y = torch.empty((n, nout), dtype=torch.float32 if out_dtype == wl.F32 else torch.int16, device="cuda")
     yb = torch.empty((n, nout), dtype=torch.int16, device="cuda") if y2 else None
@@ -100,34 +101,65 @@ def test_gemv_parity(H, orc, wdt, xdt, rows, cols, n, silu, res, out):
 
 
 MFMA_CASES = [
-    # (family, w dtype, x dtype, rows, cols, n rows, silu, residual, out)
-    (1, wl.BF16, wl.BF16, 256, 256, 1, False, False, wl.F32),
-    (1, wl.BF16, wl.BF16, 384, 1024, 130, False, True, wl.F32),
-    (1, wl.BF16, wl.BF16, 2 * 192, 512, 257, True, False, wl.BF16),
-    (1, wl.BF16, wl.BF16, 128, 3584, 64, False, False, wl.BF16),
-    (1, wl.FP8, wl.F32, 256, 3584, 200, False, True, wl.F32),
-    (1, wl.FP8, wl.BF16, 2 * 128, 1024, 33, True, False, wl.BF16),
-    (1, wl.FP8, wl.BF16, 128, 18944, 17, False, False, wl.F32),
-    (2, wl.FP8, wl.F32, 256, 3584, 200, False, True, wl.F32),
-    (2, wl.FP8, wl.BF16, 2 * 128, 1024, 33, True, False, wl.BF16),
-    (2, wl.FP8, wl.BF16, 128, 18944, 17, False, False, wl.F32),
+    # (family, w dtype, x dtype, rows, cols, n rows, silu, residual, out, k splits)
+    (1, wl.BF16, wl.BF16, 256, 256, 1, False, False, wl.F32, 1),
+    (1, wl.BF16, wl.BF16, 384, 1024, 130, False, True, wl.F32, 1),
+    (1, wl.BF16, wl.BF16, 2 * 192, 512, 257, True, False, wl.BF16, 1),
+    (1, wl.BF16, wl.BF16, 128, 3584, 64, False, False, wl.BF16, 1),
+    (1, wl.BF16, wl.BF16, 512, 3584, 70, False, True, wl.F32, 3),
+    (1, wl.BF16, wl.BF16, 2 * 256, 2048, 90, True, False, wl.BF16, 4),
+    (1, wl.FP8, wl.F32, 256, 3584, 200, False, True, wl.F32, 1),
+    (1, wl.FP8, wl.BF16, 2 * 128, 1024, 33, True, False, wl.BF16, 1),
+    (1, wl.FP8, wl.BF16, 128, 18944, 17, False, False, wl.F32, 6),
+    (2, wl.FP8, wl.F32, 256, 3584, 200, False, True, wl.F32, 1),
+    (2, wl.FP8, wl.BF16, 2 * 128, 1024, 33, True, False, wl.BF16, 1),
+    (2, wl.FP8, wl.BF16, 128, 18944, 17, False, False, wl.F32, 2),
+    # enough tiles that the 256-row activation tile is chosen (ragged in rows)
+    (1, wl.BF16, wl.BF16, 16384, 512, 1100, False, True, wl.F32, 1),
+    (1, wl.BF16, wl.BF16, 2 * 8192, 512, 1030, True, False, wl.BF16, 1),
+    (1, wl.BF16, wl.BF16, 2 * 4096, 1024, 513, True, False, wl.BF16, 3),
+    (1, wl.FP8, wl.BF16, 16384, 1024, 777, False, False, wl.F32, 1),
+    (2, wl.FP8, wl.F32, 8192, 2048, 600, False, True, wl.F32, 4),
+    (2, wl.FP8, wl.BF16, 2 * 8192, 1024, 1000, True, False, wl.BF16, 1),
 ]
 
+# the oracle checks a spread of rows of the big cases (first, last, ragged tail)
+def sample_rows(n):
+    if n <= 300:
+        return np.arange(n)
+    g = np.random.default_rng(n)
+    return np.unique(np.concatenate([[0, 1, n - 1, n - 2], g.choice(n, 28, replace=False)]))
 
-@pytest.mark.parametrize("fam,wdt,xdt,rows,cols,n,silu,res,out", MFMA_CASES)
-def test_mfma_parity(H, orc, fam, wdt, xdt, rows, cols, n, silu, res, out):
+
+@pytest.mark.parametrize("fam,wdt,xdt,rows,cols,n,silu,res,out,S", MFMA_CASES)
+def test_mfma_parity(H, orc, fam, wdt, xdt, rows, cols, n, silu, res, out, S):
     seed = rows + cols + n + 7
     W, s = make_w(rows, cols, wdt, seed)
     x = make_x(n, cols, xdt, seed)
     residual = torch.randn((n, rows)) if res else None
-    y, yb = run_proj(H, W, rows, cols, wdt, s, fam, x, xdt, n, out, silu, residual, y2=True)
-    want = oracle_proj(orc, W, wdt, s, x, xdt, 1, silu, residual)
-    got = H.values(y, out)
+    y, yb = run_proj(H, W, rows, cols, wdt, s, fam, x, xdt, n, out, silu, residual, y2=True, k_splits=S)
+    idx = sample_rows(n)
+    want = oracle_proj(orc, W, wdt, s, x[idx], xdt, 1, silu, None if residual is None else residual[idx])
+    got = H.values(y, out)[idx]
     e = H.rel_err(got, want)
-    print(f"mfma family {fam} w{wdt} x{xdt} {rows}x{cols} n={n} silu={silu}: {e:.2e}")
+    print(f"mfma family {fam} w{wdt} x{xdt} {rows}x{cols} n={n} silu={silu} S={S}: {e:.2e}")
     assert e <= (TOL if out == wl.F32 else TOL_BF16)
     if fam == 1 and out == wl.F32:
         assert e <= 2e-6  # products exact and sums fp32-accurate
+    assert H.rel_err(H.values(yb, wl.BF16)[idx], want) <= TOL_BF16
+
+
+def test_mfma_tile_height_invariance(H):
+    """A large batch runs on the 256-row activation tile and a small one on the
+    128-row tile; a row's outputs are bit-identical either way."""
+    rows, cols = 16384, 512
+    W, s = make_w(rows, cols, wl.BF16, 11)
+    x = make_x(1100, cols, wl.BF16, 12)
+    full, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, 1, x, wl.BF16, 1100, wl.F32)
+    full = full.cpu()
+    for r, n in [(0, 3), (255, 2), (1097, 3), (600, 40)]:
+        part, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, 1, x[r:r + n], wl.BF16, n, wl.F32)
+        assert torch.equal(part.cpu(), full[r:r + n]), (r, n)
 
 
 @pytest.mark.parametrize("family", [0, 1])

@@ -99,12 +99,13 @@ def test_06b_mixed_small_parity(H, orc):
     check(H, y, want["y"], BAR_BF16, "0.6b-mixed small y")
 
 
-@pytest.mark.parametrize("family", [wl.MFMA, wl.GEMV])
-def test_06b_mixed_batch_invariance(H, family):
+@pytest.mark.parametrize("family,hint", [(wl.MFMA, None), (wl.MFMA, 8), (wl.GEMV, None)])
+def test_06b_mixed_batch_invariance(H, family, hint):
     """Each row alone gives the bits it gives in the batch; the prefill slice
-    as one step gives the bits of the same rows run one step at a time."""
+    as one step gives the bits of the same rows run one step at a time (hint:
+    matrices split along K as an engine built for that batch would)."""
     w = wl.make("0.6b-mixed-bf16", "cpu", n_decode=24, chunk_rows=12, chunk=4, long_max=1400, family=family)
-    layer = H.GpuLayer(w)
+    layer = H.GpuLayer(w, batch_hint=hint)
     full = layer.step(H.GpuPool(w), w.seq, w.pos, w.x).cpu()
     for r in (0, 7, 23):  # decode rows alone
         one = layer.step(H.GpuPool(w), w.seq[r:r + 1], w.pos[r:r + 1], w.x[r:r + 1]).cpu()
@@ -151,7 +152,7 @@ def test_7b_b768(H, orc):
     w = wl.make("7b-b768-prefix-bf16", "cuda")
     print("workload 7b-b768-prefix-bf16", flush=True)
     pool = H.GpuPool(w)
-    layer = H.GpuLayer(w)
+    layer = H.GpuLayer(w, batch_hint=w.n_rows)
     y = layer.step(pool, w.seq, w.pos, w.x).cpu().numpy()
     rows = _sample(w, 10, seed=1)
     want = oracle_rows(orc, w, rows)
@@ -163,7 +164,7 @@ def test_7b_fp8_b4096(H, orc):
     w = wl.make("7b-b4096-fp8", "cuda")
     print("workload 7b-b4096-fp8", flush=True)
     pool = H.GpuPool(w)
-    layer = H.GpuLayer(w)
+    layer = H.GpuLayer(w, batch_hint=w.n_rows)
     y = layer.step(pool, w.seq, w.pos, w.x).cpu().numpy()
     rows = _sample(w, 8, seed=2)
     want = oracle_rows(orc, w, rows)
@@ -174,7 +175,7 @@ def test_fp8_small(H, orc):
     w = wl.make("7b-b4096-fp8", "cpu", n=64, L=100)
     print("workload 7b-fp8 small (64 rows, L 100)", flush=True)
     pool = H.GpuPool(w)
-    layer = H.GpuLayer(w)
+    layer = H.GpuLayer(w, batch_hint=64)  # split K on the long-K down projection
     y = layer.step(pool, w.seq, w.pos, w.x).cpu().numpy()
     rows = list(range(0, 64, 9))
     want = oracle_rows(orc, w, rows)
