@@ -291,7 +291,66 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     }
   };
 
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 0 && TM == 256) {
+    // Two groups of four waves (A = waves 0..3, B = waves 4..7; one of each
+    // per SIMD) run half a stage apart: while one wave of a SIMD issues the 64
+    // products of a stage back to back, the other reads its operands of the
+    // next stage from LDS, and at each barrier they swap.  B starts one
+    // barrier late; every barrier is shared by both groups.
+    //   A: M0 | C0 | M1 | C1 ...      B: - | M0 | C0 | M1 ...
+    // M(t) reads stage t (buffer t % 2) into registers; C(t) runs its products.
+    // Only A loads stages: stage t + 1 at the start of A's M(t) (stages 0, 1
+    // before the loop), into the buffer of stage t - 1, which both groups
+    // finished reading before A's M(t) began; A waits for it at the end of its
+    // C(t), so the barrier that opens M(t + 1) publishes it.
+    static_assert(STAGES == 2 && DPW == 8, "two stages of 64 blocks");
+    const bool grp_b = wave_u >= 4;
+    u32x4 wo0[WA], xo0[4], wo1[WA], xo1[4];
+    // A wave w fills LDS rows 128 w .. 128 w + 127 (blocks 16 w .. 16 w + 15):
+    // two runs of 64 consecutive global rows (gate and up halves of a slab
+    // under silu), each starting at a wave-uniform row.
+    const uint32_t run0 = (uint32_t)block_row(16 * (wave_u & 3)) * (uint32_t)kbytes;
+    const uint32_t run1 = (uint32_t)block_row(16 * (wave_u & 3) + 8) * (uint32_t)kbytes;
+    const uint32_t blk_stride = 8 * (uint32_t)kbytes;
+    const __amdgpu_buffer_rsrc_t aview = wave_u < 2 ? wview : xview;
+    auto dma_a = [&](int kt) {
+      uint8_t* base = smem + (kt % 2) * SB + 16 * 1024 * wave_u;
+      const uint32_t koff = (uint32_t)(kt0 + kt) * KT_BYTES;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        lds_load16(aview, voff, (i < 8 ? run0 : run1) + (uint32_t)(i & 7) * blk_stride + koff, base + 1024 * i);
+    };
+    if (!grp_b && nk > 0) {
+      dma_a(0);
+      if (nk > 1) {
+        dma_a(1);
+        __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
+      } else {
+        __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+      }
+    }
+    lds_barrier();
+    if (grp_b) lds_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      // M(kt)
+      if (!grp_b && kt >= 1 && kt + 1 < nk) dma_a(kt + 1);
+      const uint8_t* cur = smem + (kt % 2) * SB;
+      read_ops(cur, 0, wo0, xo0);
+      read_ops(cur, 1, wo1, xo1);
+      wait_lds_reads();
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // C(kt)
+      mma(wo0, xo0);
+      mma(wo1, xo1);
+      if (!grp_b) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!grp_b) lds_barrier();
+  } else if constexpr (MODE == 0) {
     // Ping-pong over the KS = KB / 64 k-steps of each stage: the operands of
     // step g + 1 are read into one register set while the products of step g
     // run on the other, so the matrix core does not wait on LDS.  At a stage
