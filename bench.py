@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--family", type=int, default=None, help="override the projection family")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy (known HBM bytes) for counter scaling")
     return ap.parse_args()
 
 
@@ -75,12 +77,65 @@ def step_bytes(w, elem):
     return st, flops, kv_tokens
 
 
+# Sources of each stage's kernel: a counter summary is only valid for the code
+# it was taken on.
+STAGE_SOURCES = {"attention": ["attention.hip"], "qkv": ["gemm.hip", "gemv.hip"], "wo": ["gemm.hip", "gemv.hip"],
+                 "gate_up": ["gemm.hip", "gemv.hip"], "down": ["gemm.hip", "gemv.hip"]}
+
+
+def source_hash(stage: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_decode_attn_amd", "csrc")
+    for f in STAGE_SOURCES[stage] + ["common.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per launch of the stage's kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's
+    reading for a copy of known size), or None if there is none or the kernel
+    source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash(stage):
+        return None
+    cb = float(kv["copy_bytes"])
+    f = float(kv["fetch_kib_per_dispatch"]) * cb / float(kv["copy_fetch_kib"])
+    w = float(kv["write_kib_per_dispatch"]) * cb / float(kv["copy_write_kib"])
+    return int(round(f + w))
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 4 * n, "copies": 3}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: every box here has one MI355X and the path has no "
-              f"multi-GPU leg in this build (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the decode path is a single-GPU kernel set with no "
+              f"collective leg (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
 
@@ -202,7 +257,8 @@ def main():
         peak = MFMA_PEAK_TFLOPS["bf16"] if (fam == 1 or not fp8) else MFMA_PEAK_TFLOPS["fp8"]
         achieved = sflops[dom] / stage_us[dom] / 1e6
     roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None}
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, w.name),
+                "algorithmic_bytes": int(sbytes_m[dom])}
     value = total_bytes / (ms_step * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- CPU baseline
