@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b-b768-prefix-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-t2", action="store_true", help="skip the small-batch GEMV pass")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--family", type=int, default=None, help="override the projection family")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -79,21 +80,23 @@ def step_bytes(w, elem):
 
 # Sources of each stage's kernel: a counter summary is only valid for the code
 # it was taken on.
-STAGE_SOURCES = {"attention": ["attention.hip"], "qkv": ["gemm.hip", "gemv.hip"], "wo": ["gemm.hip", "gemv.hip"],
-                 "gate_up": ["gemm.hip", "gemv.hip"], "down": ["gemm.hip", "gemv.hip"]}
+def stage_sources(stage: str, family: int) -> list:
+    if stage == "attention":
+        return ["attention.hip"]
+    return ["gemv.hip"] if family == 0 else ["gemm.hip"]
 
 
-def source_hash(stage: str) -> str:
+def source_hash(stage: str, family: int) -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_decode_attn_amd", "csrc")
-    for f in STAGE_SOURCES[stage] + ["common.h"]:
+    for f in stage_sources(stage, family) + ["common.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(stage: str, workload: str):
+def measured_traffic(stage: str, workload: str, family: int):
     """HBM bytes per launch of the stage's kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's
     reading for a copy of known size), or None if there is none or the kernel
@@ -108,7 +111,7 @@ def measured_traffic(stage: str, workload: str):
                 continue
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != source_hash(stage):
+    if kv.get("source_sha256") != source_hash(stage, family):
         return None
     cb = float(kv["copy_bytes"])
     f = float(kv["fetch_kib_per_dispatch"]) * cb / float(kv["copy_fetch_kib"])
@@ -257,9 +260,67 @@ def main():
         peak = MFMA_PEAK_TFLOPS["bf16"] if (fam == 1 or not fp8) else MFMA_PEAK_TFLOPS["fp8"]
         achieved = sflops[dom] / stage_us[dom] / 1e6
     roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, w.name),
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, w.name, int(fam)),
                 "algorithmic_bytes": int(sbytes_m[dom])}
     value = total_bytes / (ms_step * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- T1 / T2
+    # T1: append + paged attention alone on this workload's pool and rows, cold
+    # (a 2 GiB buffer is read before every rep, outside the events, so no page
+    # is left in L2 or the 256 MB MALL; read, not written, so that no dirty
+    # lines are left to be written back during the timed call) and warm.
+    # T2: the vector-family GEMV over every weight matrix of the layer at
+    # decode batches 1..16, cold.
+    flush = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    flush_sum = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps, cold):
+        ts = []
+        for _ in range(reps):
+            if cold:
+                torch.sum(flush, 0, out=flush_sum)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+
+    ab = sbytes_m["attention"]
+    t1_res = {"bytes": int(ab)}
+    for mode in ("cold", "warm"):
+        med, p10, p90 = timed(st_append_attn, max(args.steps, 10), mode == "cold")
+        t1_res[mode] = {"us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+                    "GB_s": round(ab / med / 1e3, 1), "hbm_frac": round(ab / med / 1e3 / HBM_PEAK_GBS, 4)}
+    t2_res = None
+    if not args.no_t2 and F and w.w_dtype == 1:
+        g_layer = H.GpuLayer(w, family=0).layer  # same weights, vector family
+        t2_res = {"matrices": "W_qkv, W_o, [W_gate; W_up], W_down", "family": 0}
+        wbytes = 2 * (nqkv * D + D * nq * d + 2 * F * D + D * F)
+        for nb in (1, 4, 8, 16):
+            xs = (torch.randn((nb, max(D, F, nq * d)), device="cuda") * 0.5).to(torch.bfloat16).view(torch.int16)
+            oq = torch.empty((nb, nqkv), dtype=torch.int16, device="cuda")
+            oh = torch.empty((nb, D), dtype=torch.float32, device="cuda")
+            og = torch.empty((nb, F), dtype=torch.int16, device="cuda")
+            res = torch.zeros((nb, D), dtype=torch.float32, device="cuda")
+            xd = xs[:, :D].contiguous()
+            xa = xs[:, :nq * d].contiguous()
+            xf = xs[:, :F].contiguous()
+
+            def gemv_pass():
+                pkd.gemv_rows(g_layer.w_qkv, xd, 1, nb, oq, 1)
+                pkd.gemv_rows(g_layer.w_o, xa, 1, nb, oh, 0, residual=res)
+                pkd.gemv_rows(g_layer.w_gate_up, xd, 1, nb, og, 1, silu_pair=True)
+                pkd.gemv_rows(g_layer.w_down, xf, 1, nb, oh, 0, residual=res)
+            for _ in range(3):
+                gemv_pass()
+            med, p10, p90 = timed(gemv_pass, max(args.steps, 10), True)
+            byt = wbytes + nb * 2 * (D + nq * d + D + F) + nb * (2 * nqkv + 8 * D + 2 * F + 8 * D)
+            t2_res[f"B{nb}"] = {"us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2), "bytes": int(byt),
+                            "GB_s": round(byt / med / 1e3, 1), "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4)}
+    del flush, flush_sum
 
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
@@ -295,6 +356,8 @@ def main():
         "step_bytes": int(total_bytes),
         "kernels": kernels,
         "roofline": roofline,
+        "t1_attention": t1_res,
+        "t2_gemv": t2_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

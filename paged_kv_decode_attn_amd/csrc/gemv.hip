@@ -13,7 +13,11 @@
 // projections).  Each output is a lane-sequential fp32 sum over its k-vectors
 // followed by a butterfly over the 64 lanes whose tree (pairs at distance 32,
 // 16, 8, 4, 2, 1) is the same for every R, so the result of an activation row
-// does not depend on how many rows share the launch.
+// does not depend on how many rows share the launch.  Matrices with few rows
+// (fewer than ~8K waves' worth) split K over the four waves of a block: wave w
+// takes the 1 KiB runs w, w + 4, w + 8, ... of each row and the four partial
+// sums are added through LDS in the order w = 0, 1, 2, 3.  The split is a
+// function of the matrix shape only, so it never varies with the batch.
 
 #include "common.h"
 
@@ -111,15 +115,23 @@ __device__ __forceinline__ int transpose_reduce(float (&v)[R]) {
   return row;
 }
 
+// a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs a, b (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// NR weight rows per wave (SILU: NR / 2 gate rows j and the matching up rows
-// F + j), R activation rows per launch tile (blockIdx.y), 4 waves per block.
-template <int WT, int XT, int R, int NR, bool SILU>
+// NR weight rows per row group (SILU: NR / 2 gate rows j and the matching up
+// rows F + j), R activation rows per launch tile (blockIdx.y), 4 waves per
+// block: 4 row groups (KS = 1) or one row group split over K (KS = 4).
+template <int WT, int XT, int R, int NR, bool SILU, int KS>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
   constexpr int E = WV<WT>::E;
-  constexpr int NP = SILU ? NR / 2 : NR;  // outputs per wave
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int NP = SILU ? NR / 2 : NR;  // outputs per row group
+  const int wib = threadIdx.x >> 6;
+  const int kw = KS == 1 ? 0 : wib;                               // k-slice of this wave
+  const int wave = KS == 1 ? blockIdx.x * 4 + wib : blockIdx.x;   // row group
   const int l = lane_id();
   const int o0 = wave * NP;  // first output of this wave
   if (o0 >= P.n_out) return;
@@ -140,11 +152,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
   constexpr int U = 4;  // k-vectors per lane in flight per row
-  for (int j0 = l; j0 < nvec; j0 += 64 * U) {
+  for (int j0 = 64 * kw + l; j0 < nvec; j0 += 64 * KS * U) {
     u32x4 wv[U][NR];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = j0 + 64 * u;
+      const int j = j0 + 64 * KS * u;
 #pragma unroll
       for (int i = 0; i < NR; ++i)
         wv[u][i] = j < nvec ? *reinterpret_cast<const u32x4*>(P.W + wrow[i] * row_bytes + 16 * (int64_t)j)
@@ -152,8 +164,28 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = j0 + 64 * u;
+      const int j = j0 + 64 * KS * u;
       if (j >= nvec) break;
+      if constexpr (WT == 1 && XT == 1) {
+        // bf16 x bf16: the packed pairs go straight into the dot-2 instruction
+        // (exact products, fp32 sums), pairs (0,1), (2,3), (4,5), (6,7) in order
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r0 + r >= P.n_rows) break;
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(P.x) +
+                                                           (int64_t)(r0 + r) * P.x_stride + 8 * j);
+#pragma unroll
+          for (int i = 0; i < NR; ++i) {
+            float a = acc[i][r];
+            a = dot2_bf16(wv[u][i].x, xv.x, a);
+            a = dot2_bf16(wv[u][i].y, xv.y, a);
+            a = dot2_bf16(wv[u][i].z, xv.z, a);
+            a = dot2_bf16(wv[u][i].w, xv.w, a);
+            acc[i][r] = a;
+          }
+        }
+        continue;
+      }
       float w[NR][E];
 #pragma unroll
       for (int i = 0; i < NR; ++i) decode_w<WT>(wv[u][i], w[i]);
@@ -171,13 +203,29 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
   }
   int row = 0;
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    row = transpose_reduce<R>(acc[i]);
-    acc[i][0] *= P.w_scale;
-  }
+  for (int i = 0; i < NR; ++i) row = transpose_reduce<R>(acc[i]);
   // one writer lane per activation row: the lane whose low bits are zero
   constexpr int LOG_R = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : R == 8 ? 3 : 4;
   const bool writer = (l & ((64 >> LOG_R) - 1)) == 0;
+  if constexpr (KS > 1) {
+    // the four k-slices' partial sums, added in slice order by wave 0
+    __shared__ float part[KS][NR][R];
+    if (writer) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) part[kw][i][row] = acc[i][0];
+    }
+    __syncthreads();
+    if (kw != 0) return;
+    if (writer) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        float t = part[0][i][row];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) t += part[w][i][row];
+        acc[i][0] = t;
+      }
+    }
+  }
   const int r = r0 + row;
   if (!writer || r >= P.n_rows) return;
 #pragma unroll
@@ -186,9 +234,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
     if (o >= P.n_out) break;
     float v;
     if constexpr (SILU) {
-      v = silu(acc[i][0]) * acc[NP + i][0];
+      v = silu(acc[i][0] * P.w_scale) * (acc[NP + i][0] * P.w_scale);
     } else {
-      v = acc[i][0];
+      v = acc[i][0] * P.w_scale;
       if (P.residual) v += P.residual[(int64_t)r * P.n_out + o];
     }
     if (P.y_bf16) reinterpret_cast<uint16_t*>(P.y)[(int64_t)r * P.y_stride + o] = (uint16_t)f32_to_bf16_bits(v);
@@ -197,13 +245,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
   }
 }
 
+// K split of a matrix: 4 when its row groups alone would give fewer than
+// 8192 waves (a function of the shape, never of the batch).
+static int gemv_k_split(int n_out, int np) { return (n_out + np - 1) / np < 8192 ? 4 : 1; }
+
 template <int WT, int XT, int R, bool SILU>
 static void launch_r(const GemvParams& P, hipStream_t st) {
   constexpr int NR = 4;
   constexpr int NP = SILU ? NR / 2 : NR;
-  const int waves = (P.n_out + NP - 1) / NP;
-  dim3 grid((waves + 3) / 4, (P.n_rows + R - 1) / R);
-  hipLaunchKernelGGL((gemv_kernel<WT, XT, R, NR, SILU>), grid, dim3(256), 0, st, P);
+  const int groups = (P.n_out + NP - 1) / NP;
+  if (gemv_k_split(P.n_out, NP) > 1) {
+    dim3 grid(groups, (P.n_rows + R - 1) / R);
+    hipLaunchKernelGGL((gemv_kernel<WT, XT, R, NR, SILU, 4>), grid, dim3(256), 0, st, P);
+  } else {
+    dim3 grid((groups + 3) / 4, (P.n_rows + R - 1) / R);
+    hipLaunchKernelGGL((gemv_kernel<WT, XT, R, NR, SILU, 1>), grid, dim3(256), 0, st, P);
+  }
 }
 
 template <int WT, int XT, bool SILU>
