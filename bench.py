@@ -156,7 +156,8 @@ def main():
     B, D, nq, nkv, d, F = w.n_rows, w.hidden, w.n_q, w.n_kv, w.head_dim, w.ffn
     stream = torch.cuda.current_stream()
     s_t, p_t = H.rows_tensors(w.seq, w.pos)
-    rows = pkd.make_rows(s_t, p_t)
+    distinct = len(set(w.seq.tolist())) == B  # pure decode batch: the append runs inside attention
+    rows = pkd.make_rows(s_t, p_t, distinct)
     x = w.x.contiguous()
     y = torch.empty((B, D), dtype=torch.float32, device="cuda")
     ws = H.aligned_empty(pkd.pkd_step_workspace_bytes(L, pool.handle, B))

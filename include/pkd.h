@@ -213,11 +213,20 @@ pkd_status pkd_pool_check(pkd_pool* pool, pkd_stream stream, pkd_error* err);
  * without running out of cache": every step is a set of rows carrying token,
  * sequence and position; [LRS] section 1: steps mix prefill and decode).
  * seq and pos are device arrays of n int32.
+ * flags: 0, or PKD_ROWS_DISTINCT_SEQS when the caller guarantees that no
+ * sequence has more than one row in the call (a pure decode batch).  Then the
+ * append of each row's key and value runs inside the attention kernel instead
+ * of a separate pass before it; results are bit-identical either way.  If the
+ * guarantee is broken, a later row of a repeated sequence may miss an earlier
+ * row's token (no memory is touched out of bounds).
  */
+enum { PKD_ROWS_DISTINCT_SEQS = 1 };
+
 typedef struct {
   const int32_t* seq;
   const int32_t* pos;
   int32_t n;
+  int32_t flags;
 } pkd_rows;
 
 /* ------------------------------------------------------------------------ */

@@ -51,8 +51,12 @@ class pkd_pool_info(ctypes.Structure):
                 ("counts_offset", ctypes.c_size_t), ("error_offset", ctypes.c_size_t)]
 
 
+ROWS_DISTINCT_SEQS = 1
+
+
 class pkd_rows(ctypes.Structure):
-    _fields_ = [("seq", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("n", ctypes.c_int32)]
+    _fields_ = [("seq", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("n", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 class pkd_matrix(ctypes.Structure):
@@ -179,8 +183,8 @@ def pkd_pool_check(pool, stream=None) -> None:
 
 
 # ------------------------------------------------------------------ attention
-def make_rows(seq: torch.Tensor, pos: torch.Tensor) -> pkd_rows:
-    return pkd_rows(_ptr(seq), _ptr(pos), int(seq.numel()))
+def make_rows(seq: torch.Tensor, pos: torch.Tensor, distinct: bool = False) -> pkd_rows:
+    return pkd_rows(_ptr(seq), _ptr(pos), int(seq.numel()), ROWS_DISTINCT_SEQS if distinct else 0)
 
 
 def pkd_attn_workspace_bytes(pool, n_q_heads: int, max_rows: int) -> int:

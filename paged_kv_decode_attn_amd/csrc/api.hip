@@ -105,6 +105,8 @@ static pkd_status validate_rows(const pkd_rows* rows, pkd_error* err) {
   if (rows->n < 0) return fail(err, PKD_ERR_INVALID_ARG, rows->n, 0, "negative row count %d", rows->n);
   if (rows->n > 0 && (!rows->seq || !rows->pos))
     return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "rows->seq / rows->pos is NULL");
+  if (rows->flags & ~PKD_ROWS_DISTINCT_SEQS)
+    return fail(err, PKD_ERR_INVALID_ARG, rows->flags, PKD_ROWS_DISTINCT_SEQS, "unknown rows->flags bits");
   return PKD_OK;
 }
 
@@ -320,6 +322,7 @@ pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_h
   a.pool = pool;
   a.seq = rows->seq;
   a.pos = rows->pos;
+  a.distinct = (rows->flags & PKD_ROWS_DISTINCT_SEQS) != 0;
   a.n_rows = rows->n;
   a.n_q_heads = n_q_heads;
   a.q = q;
@@ -503,6 +506,7 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   a.pool = pool;
   a.seq = rows->seq;
   a.pos = rows->pos;
+  a.distinct = (rows->flags & PKD_ROWS_DISTINCT_SEQS) != 0;
   a.n_rows = n;
   a.n_q_heads = nq;
   const int es = elem_size(act);

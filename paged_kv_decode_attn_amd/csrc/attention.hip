@@ -58,6 +58,11 @@ struct AttnParams {
   int32_t* counter;            // chunked: work counter
   float* part_ml;              // chunked: [units * n_kv * G][2]  (m, l)
   float* part_o;               // chunked: [units * n_kv * G][d]
+  const void* new_k;           // [n_rows][n_kv][d] in q's dtype, or null
+  const void* new_v;
+  int64_t new_stride;          // elements between rows of new_k / new_v
+  float enc_k_scale;           // fp8 pool: codes = E4M3(value / scale)
+  float enc_v_scale;
 };
 
 // Per-KV-dtype geometry.  kvt: 0 f32, 1 bf16, 2 fp8.  NL = 16-byte loads per lane
@@ -83,11 +88,20 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_ca
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// First block-table window of sequence s (lane i: logical page i), read in
+// the same round trip as the page count; zeros for an out-of-range sequence.
+__device__ __forceinline__ void row_meta(const AttnParams& P, int s, int& count, int& tab) {
+  const bool s_ok = s >= 0 && s < P.max_seqs;
+  const int l = lane_id();
+  count = s_ok ? P.counts[s] : 0;
+  tab = (s_ok && l < P.max_pages) ? P.table[(int64_t)s * P.max_pages + l] : 0;
+}
+
 // Row validity and context length; sets the sticky error word on a bad row.
-__device__ __forceinline__ bool row_ok(const AttnParams& P, int s, int p, bool report) {
+__device__ __forceinline__ bool row_ok(const AttnParams& P, int s, int p, int count, bool report) {
   unsigned e = 0;
   if (s < 0 || s >= P.max_seqs) e = kErrSeq;
-  else if (p < 0 || p >= kPage * P.counts[s]) e = kErrPos;
+  else if (p < 0 || p >= kPage * count) e = kErrPos;
   if (e && report && lane_id() == 0) atomicOr(P.err, e);
   return e == 0;
 }
@@ -247,18 +261,6 @@ __device__ __forceinline__ void page_pv(const PageRegs<KVT, D>& vr, const float 
   }
 }
 
-template <int KVT, int D>
-__device__ __forceinline__ void load_page(const uint8_t* kb, PageRegs<KVT, D>& kr,
-                                          PageRegs<KVT, D>& vr, uint32_t block_bytes) {
-  using GE = Geo<KVT, D>;
-  const uint8_t* k = kb + 16 * lane_id();
-  const uint8_t* v = k + block_bytes;
-#pragma unroll
-  for (int j = 0; j < GE::NL; ++j) kr[j] = load16(k + 1024 * j);
-#pragma unroll
-  for (int j = 0; j < GE::NL; ++j) vr[j] = load16(v + 1024 * j);
-}
-
 // State of one work unit's online softmax.
 template <int KVT, int D>
 struct Acc {
@@ -267,16 +269,12 @@ struct Acc {
   float l;  // this lane's partial sum of weights
 };
 
-// Processes one page into the accumulators.
+// Online-softmax update of one page from its scores; returns the weights p.
 template <int KVT, int D>
-__device__ __forceinline__ void page_step(const AttnParams& P, Acc<KVT, D>& A, const PageRegs<KVT, D>& kr,
-                                          PageRegs<KVT, D>& vr, const QRegs<KVT, D>& qv,
-                                          const QFRegs<KVT, D>& qf, int pg, int p_row) {
+__device__ __forceinline__ void page_softmax(const AttnParams& P, Acc<KVT, D>& A, const f32x4_t (&S)[2], int pg,
+                                             int p_row, bool (&valid)[2][4], float (&p)[2][4]) {
   using GE = Geo<KVT, D>;
   const int grp = lane_id() >> 4;
-  f32x4_t S[2];
-  page_scores<KVT, D>(kr, qv, qf, S);
-  bool valid[2][4];
   float s[2][4];
   float mx = -INFINITY;
   const int t0 = pg * kPage + 4 * grp;
@@ -292,7 +290,6 @@ __device__ __forceinline__ void page_step(const AttnParams& P, Acc<KVT, D>& A, c
   mx = fmaxf(mx, shfl_xor(mx, 32));
   const float m_new = fmaxf(A.m, mx);
   const float alpha = exp2f(A.m - m_new);
-  float p[2][4];
   float ls = 0.f;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -305,15 +302,80 @@ __device__ __forceinline__ void page_step(const AttnParams& P, Acc<KVT, D>& A, c
   A.m = m_new;
 #pragma unroll
   for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] *= alpha;
-  if ((pg + 1) * kPage > p_row + 1) mask_v<KVT, D>(vr, valid);  // partial last page
-  page_pv<KVT, D>(vr, p, A.O);
 }
 
-// Runs pages [pg0, pg1) of row r, kv head g.  Loads of the next page are issued
-// before the current page is reduced.
 template <int KVT, int D>
+__device__ __forceinline__ void load_block(const uint8_t* b, PageRegs<KVT, D>& r) {
+  using GE = Geo<KVT, D>;
+  const uint8_t* k = b + 16 * lane_id();
+#pragma unroll
+  for (int j = 0; j < GE::NL; ++j) r[j] = load16(k + 1024 * j);
+}
+
+// Row r's own key and value for kv head g, as the pool stores them: lane l
+// holds dims l and l + 64 (and so on) of each, already converted to the pool
+// dtype (bits in the low bytes).  Loaded early; stored by append_store.
+template <int KVT, int D>
+struct NewToken {
+  static constexpr int PER = (D + kWave - 1) / kWave;
+  uint32_t k[PER], v[PER];
+};
+
+template <int KVT, int D>
+__device__ __forceinline__ void append_load(const AttnParams& P, int r, int g, NewToken<KVT, D>& nt) {
+  const int l = lane_id();
+  const int64_t src = (int64_t)r * P.new_stride + (int64_t)g * D;
+#pragma unroll
+  for (int j = 0; j < NewToken<KVT, D>::PER; ++j) {
+    const int c = l + kWave * j;
+    if (c >= D) break;
+    if constexpr (KVT == 0) {
+      nt.k[j] = __float_as_uint(reinterpret_cast<const float*>(P.new_k)[src + c]);
+      nt.v[j] = __float_as_uint(reinterpret_cast<const float*>(P.new_v)[src + c]);
+    } else {
+      nt.k[j] = reinterpret_cast<const uint16_t*>(P.new_k)[src + c];
+      nt.v[j] = reinterpret_cast<const uint16_t*>(P.new_v)[src + c];
+    }
+  }
+}
+
+// Writes the token at slot t of physical page `page`, in the layout of
+// include/pkd.h; fp8 pools take E4M3 RNE of value / scale (fp32 division),
+// saturating.
+template <int KVT, int D>
+__device__ __forceinline__ void append_store(const AttnParams& P, int g, int page, int t,
+                                             const NewToken<KVT, D>& nt) {
+  uint8_t* kb = const_cast<uint8_t*>(P.pages) + (uint64_t)page * P.page_stride + (uint64_t)g * 2 * P.block_bytes;
+  uint8_t* vb = kb + P.block_bytes;
+  const int l = lane_id();
+  const int a = t / 16, b = (t % 16) / 4, i = t % 4;
+#pragma unroll
+  for (int j = 0; j < NewToken<KVT, D>::PER; ++j) {
+    const int c = l + kWave * j;
+    if (c >= D) break;
+    if constexpr (KVT == 0) {
+      reinterpret_cast<uint32_t*>(kb)[((t / 16) * (D / 4) + c / 4) * 64 + (t % 16) * 4 + c % 4] = nt.k[j];
+      reinterpret_cast<uint32_t*>(vb)[(((a * (D / 16) + c / 16) * 4 + b) * 16 + c % 16) * 4 + i] = nt.v[j];
+    } else if constexpr (KVT == 1) {
+      reinterpret_cast<uint16_t*>(kb)[((t / 16) * (D / 8) + c / 8) * 128 + (t % 16) * 8 + c % 8] = (uint16_t)nt.k[j];
+      reinterpret_cast<uint16_t*>(vb)[(((c / 16) * 4 + b) * 16 + c % 16) * 8 + 4 * a + i] = (uint16_t)nt.v[j];
+    } else {
+      const unsigned codes = f32x2_to_fp8x2(bf16_bits_to_f32(nt.k[j]) / P.enc_k_scale,
+                                            bf16_bits_to_f32(nt.v[j]) / P.enc_v_scale);
+      kb[((t / 16) * (D / 16) + c / 16) * 256 + (t % 16) * 16 + c % 16] = (uint8_t)(codes & 0xff);
+      vb[(((c / 32) * 4 + b) * 16 + c % 16) * 16 + 8 * ((c / 16) % 2) + 4 * a + i] = (uint8_t)(codes >> 8);
+    }
+  }
+}
+
+// Runs pages [pg0, pg1) of row r, kv head g.  One K and one V block live in
+// registers: the next page's K is requested as soon as the score products have
+// consumed the current K, and its V once the P.V products have consumed the
+// current V, so a wave keeps about one page in flight with half the registers
+// of a double buffer and three waves fit on a SIMD.
+template <int KVT, int D, bool FUSE = false>
 __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, int r, int s, int p_row, int g,
-                                         int pg0, int pg1) {
+                                         int pg0, int pg1, int tab) {
   using GE = Geo<KVT, D>;
   u32x4 qv[GE::NQ];
   float qf[GE::NQ];
@@ -324,16 +386,46 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
   A.l = 0.f;
   const int32_t* trow = P.table + (int64_t)s * P.max_pages;
   const uint8_t* base = P.pages + (uint64_t)g * 2 * P.block_bytes;
-  u32x4 k0[GE::NL], v0[GE::NL], k1[GE::NL], v1[GE::NL];
-  load_page<KVT, D>(base + (uint64_t)trow[pg0] * P.page_stride, k0, v0, P.block_bytes);
-  int pg = pg0;
-  for (; pg + 1 < pg1; pg += 2) {
-    load_page<KVT, D>(base + (uint64_t)trow[pg + 1] * P.page_stride, k1, v1, P.block_bytes);
-    page_step<KVT, D>(P, A, k0, v0, qv, qf, pg, p_row);
-    if (pg + 2 < pg1) load_page<KVT, D>(base + (uint64_t)trow[pg + 2] * P.page_stride, k0, v0, P.block_bytes);
-    page_step<KVT, D>(P, A, k1, v1, qv, qf, pg + 1, p_row);
+  // lane i holds the physical page of logical page win + i (tab: the caller's
+  // window at pg0): the unit's table entries arrive in one load instead of one
+  // dependent load per page
+  int win = pg0;
+  auto page_of = [&](int pg) {
+    if (pg - win >= kWave) {
+      win += kWave;
+      tab = win + lane_id() < pg1 ? trow[win + lane_id()] : 0;
+    }
+    return __shfl(tab, pg - win, kWave);
+  };
+  // FUSE: the row's own token is stored into its page here, and every load of
+  // that page waits for the stores (vmcnt(0) covers this wave's stores), so
+  // the page is read exactly as a separate append pass would leave it.  No
+  // other wave of the launch reads that page.
+  const int own = FUSE ? p_row / kPage : -1;
+  NewToken<KVT, D> nt;
+  if constexpr (FUSE) append_load<KVT, D>(P, r, g, nt);
+  u32x4 kr[GE::NL], vr[GE::NL];
+  const uint8_t* cur = base + (uint64_t)page_of(pg0) * P.page_stride;
+  if (FUSE && own == pg0) {
+    append_store<KVT, D>(P, g, page_of(own), p_row % kPage, nt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  if (pg < pg1) page_step<KVT, D>(P, A, k0, v0, qv, qf, pg, p_row);
+  load_block<KVT, D>(cur, kr);
+  load_block<KVT, D>(cur + P.block_bytes, vr);
+  if (FUSE && own != pg0) append_store<KVT, D>(P, g, page_of(own), p_row % kPage, nt);
+  for (int pg = pg0; pg < pg1; ++pg) {
+    const uint8_t* nxt = pg + 1 < pg1 ? base + (uint64_t)page_of(pg + 1) * P.page_stride : nullptr;
+    f32x4_t S[2];
+    page_scores<KVT, D>(kr, qv, qf, S);
+    if (FUSE && pg + 1 == own) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (nxt) load_block<KVT, D>(nxt, kr);
+    bool valid[2][4];
+    float p[2][4];
+    page_softmax<KVT, D>(P, A, S, pg, p_row, valid, p);
+    if ((pg + 1) * kPage > p_row + 1) mask_v<KVT, D>(vr, valid);  // partial last page
+    page_pv<KVT, D>(vr, p, A.O);
+    if (nxt) load_block<KVT, D>(nxt + P.block_bytes, vr);
+  }
 }
 
 // Sum of the lane-partial l over the four 16-lane groups (fixed butterfly).
@@ -378,16 +470,20 @@ __device__ __forceinline__ void zero_heads(const AttnParams& P, int r, int g) {
 }
 
 // One wave per (row, kv head); every row is a single chunk.
-template <int KVT, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_direct_kernel(AttnParams P) {
+//   FUSE: every sequence has one row in the launch; the wave also appends its
+//   row's token (see run_unit).
+template <int KVT, int D, bool FUSE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attn_direct_kernel(AttnParams P) {
   const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
   const int s = P.seq[r], p = P.pos[r];
-  if (!row_ok(P, s, p, g == 0)) {
+  int count, tab;
+  row_meta(P, s, count, tab);
+  if (!row_ok(P, s, p, count, g == 0)) {
     zero_heads<D>(P, r, g);
     return;
   }
   Acc<KVT, D> A;
-  run_unit<KVT, D>(P, A, r, s, p, g, 0, (p + kPage) / kPage);
+  run_unit<KVT, D, FUSE>(P, A, r, s, p, g, 0, (p + kPage) / kPage, tab);
   finish<KVT, D>(P, A, r, g);
 }
 
@@ -455,8 +551,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     const int s = P.seq[r], p = P.pos[r];
     const int npg = (p + kPage) / kPage;
     const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
+    const int tab = pg0 + l < pg1 ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
     Acc<KVT, D> A;
-    run_unit<KVT, D>(P, A, r, s, p, g, pg0, pg1);
+    run_unit<KVT, D>(P, A, r, s, p, g, pg0, pg1, tab);
     if (nch == 1) {
       finish<KVT, D>(P, A, r, g);
       continue;
@@ -521,55 +618,17 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
 }
 
 // ------------------------------------------------------------------ append
-// Writes each row's own key and value at (seq, pos), converted to the pool
-// dtype, into the layout of include/pkd.h.  One wave per (row, kv head).
+// One wave per (row, kv head); every append lands before the attention
+// kernel that follows on the stream reads the pool.
 template <int KVT, int D>
-__global__ __launch_bounds__(64) void append_kernel(AttnParams P, const void* k_new, const void* v_new,
-                                                    int64_t kv_stride, float inv_k, float inv_v, float k_scale,
-                                                    float v_scale) {
+__global__ __launch_bounds__(64) void append_kernel(AttnParams P) {
   const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
   const int s = P.seq[r], p = P.pos[r];
-  if (!row_ok(P, s, p, g == 0)) return;
-  const int page = P.table[(int64_t)s * P.max_pages + p / kPage];
-  const int t = p % kPage;
-  uint8_t* kb = const_cast<uint8_t*>(P.pages) + (uint64_t)page * P.page_stride + (uint64_t)g * 2 * P.block_bytes;
-  uint8_t* vb = kb + P.block_bytes;
-  const int l = lane_id();
-  const int64_t src = (int64_t)r * kv_stride + (int64_t)g * D;
-  (void)inv_k; (void)inv_v; (void)k_scale; (void)v_scale;
-  if constexpr (KVT == 0) {
-    const float* kn = reinterpret_cast<const float*>(k_new) + src;
-    const float* vn = reinterpret_cast<const float*>(v_new) + src;
-    float* K = reinterpret_cast<float*>(kb);
-    float* V = reinterpret_cast<float*>(vb);
-    for (int c = l; c < D; c += kWave) {
-      K[((t / 16) * (D / 4) + c / 4) * 64 + (t % 16) * 4 + c % 4] = kn[c];
-      const int a = t / 16, b = (t % 16) / 4, i = t % 4;
-      V[(((a * (D / 16) + c / 16) * 4 + b) * 16 + c % 16) * 4 + i] = vn[c];
-    }
-  } else if constexpr (KVT == 1) {
-    const uint16_t* kn = reinterpret_cast<const uint16_t*>(k_new) + src;
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(v_new) + src;
-    uint16_t* K = reinterpret_cast<uint16_t*>(kb);
-    uint16_t* V = reinterpret_cast<uint16_t*>(vb);
-    for (int c = l; c < D; c += kWave) {
-      K[((t / 16) * (D / 8) + c / 8) * 128 + (t % 16) * 8 + c % 8] = kn[c];
-      const int a = t / 16, b = (t % 16) / 4, i = t % 4;
-      V[(((c / 16) * 4 + b) * 16 + c % 16) * 8 + 4 * a + i] = vn[c];
-    }
-  } else {
-    const uint16_t* kn = reinterpret_cast<const uint16_t*>(k_new) + src;
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(v_new) + src;
-    for (int c = l; c < D; c += kWave) {
-      // value / scale in fp32 (true division), then E4M3 RNE with saturation
-      const float kq = bf16_bits_to_f32(kn[c]) / k_scale;
-      const float vq = bf16_bits_to_f32(vn[c]) / v_scale;
-      const unsigned codes = f32x2_to_fp8x2(kq, vq);
-      kb[((t / 16) * (D / 16) + c / 16) * 256 + (t % 16) * 16 + c % 16] = (uint8_t)(codes & 0xff);
-      const int a = t / 16, b = (t % 16) / 4, i = t % 4;
-      vb[(((c / 32) * 4 + b) * 16 + c % 16) * 16 + 8 * ((c / 16) % 2) + 4 * a + i] = (uint8_t)(codes >> 8);
-    }
-  }
+  const int count = (s >= 0 && s < P.max_seqs) ? P.counts[s] : 0;
+  if (!row_ok(P, s, p, count, g == 0)) return;
+  NewToken<KVT, D> nt;
+  append_load<KVT, D>(P, r, g, nt);
+  append_store<KVT, D>(P, g, P.table[(int64_t)s * P.max_pages + p / kPage], p % kPage, nt);
 }
 
 // ------------------------------------------------------------------ host
@@ -624,13 +683,13 @@ template <int KVT, int D>
 static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk,
                        hipStream_t st) {
   const int units = a.n_rows * n_kv;
-  if (a.k_new) {
-    const float ks = a.pool->desc.k_scale, vs = a.pool->desc.v_scale;
-    hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P, a.k_new, a.v_new, a.kv_new_stride,
-                       1.0f / ks, 1.0f / vs, ks, vs);
+  if (!chunk && a.k_new && a.distinct) {
+    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true>), dim3(units), dim3(64), 0, st, P);
+    return;
   }
+  if (a.k_new) hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
   if (!chunk) {
-    hipLaunchKernelGGL((attn_direct_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
+    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false>), dim3(units), dim3(64), 0, st, P);
     return;
   }
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, st, P, w.row_chunks);
@@ -678,6 +737,11 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   P.counter = w.counter;
   P.part_ml = w.part_ml;
   P.part_o = w.part_o;
+  P.new_k = a.k_new;
+  P.new_v = a.v_new;
+  P.new_stride = a.kv_new_stride;
+  P.enc_k_scale = d.k_scale;
+  P.enc_v_scale = d.v_scale;
   const bool ch = chunked(pool);
   const int kvt = d.kv_dtype;
   if (d.head_dim == 128) {

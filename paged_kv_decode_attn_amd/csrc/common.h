@@ -110,6 +110,7 @@ struct AttnArgs {
   void* out;
   int32_t out_dtype;
   int64_t out_stride;
+  int32_t distinct;  // no sequence has two rows: the append may run inside attention
 };
 size_t attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t max_rows);
 pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err);

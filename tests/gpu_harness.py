@@ -77,11 +77,11 @@ def rows_tensors(seq, pos):
 
 
 def run_attention(pool: GpuPool, seq, pos, q: torch.Tensor, k_new=None, v_new=None,
-                  out_dtype: int = wl.F32) -> torch.Tensor:
+                  out_dtype: int = wl.F32, distinct: bool = False) -> torch.Tensor:
     w = pool.w
     s, p = rows_tensors(seq, pos)
     n = s.numel()
-    rows = pkd.make_rows(s, p)
+    rows = pkd.make_rows(s, p, distinct)
     ws = aligned_empty(pkd.pkd_attn_workspace_bytes(pool.handle, w.n_q, n))
     out = torch.empty((n, w.n_q, w.head_dim), dtype=torch.float32 if out_dtype == wl.F32 else torch.int16,
                       device=DEV)
@@ -113,7 +113,8 @@ class GpuLayer:
     def step(self, pool: GpuPool, seq, pos, x: torch.Tensor, ws: torch.Tensor | None = None):
         s, p = rows_tensors(seq, pos)
         n = s.numel()
-        rows = pkd.make_rows(s, p)
+        distinct = len(set(np.asarray(seq).tolist())) == n  # pure decode batch: append fused into attention
+        rows = pkd.make_rows(s, p, distinct)
         if ws is None:
             ws = aligned_empty(pkd.pkd_step_workspace_bytes(self.layer, pool.handle, n))
         y = torch.empty((n, self.w.hidden), dtype=torch.float32, device=DEV)

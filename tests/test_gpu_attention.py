@@ -76,6 +76,43 @@ def test_attention_parity(H, orc, kvt, nq, nkv, d, append, chunk):
         assert np.array_equal(gb, torch.from_numpy(got).float().to(torch.bfloat16).double().numpy())
 
 
+FUSED_CASES = [
+    # (kv dtype, n_q, n_kv, d): the append inside the attention kernel
+    (wl.F32, 4, 2, 64),
+    (wl.BF16, 4, 2, 128),
+    (wl.BF16, 14, 2, 128),
+    (wl.BF16, 32, 2, 64),
+    (wl.FP8, 14, 2, 128),
+    (wl.FP8, 4, 2, 64),
+]
+
+
+@pytest.mark.parametrize("kvt,nq,nkv,d", FUSED_CASES)
+def test_fused_append_bit_identical(H, kvt, nq, nkv, d):
+    """With every sequence appearing once, the append runs inside the attention
+    kernel (the row's token substituted in registers).  Outputs and the pool
+    bytes it leaves are bit-identical to the separate append followed by
+    attention, for a token in every one of the 32 page slots."""
+    lens = tuple(range(1, 41)) + (63, 64, 65, 96, 97, 128, 129)
+    w = wl.make("attn", "cpu", seed=40 + nq + d + kvt, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens,
+                append=True, chunk=8)
+    dev = lambda t: t.to("cuda")
+    outs, pools = [], []
+    for distinct in (False, True):
+        pool = H.GpuPool(w)
+        outs.append(H.run_attention(pool, w.seq, w.pos, dev(w.q), dev(w.k_new), dev(w.v_new), wl.F32,
+                                    distinct=distinct).cpu())
+        pools.append(pool.pages_bytes().cpu())
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(pools[0], pools[1])
+    # and a shuffled batch through the fused path gives the same bits per row
+    perm = np.random.default_rng(5).permutation(w.n_rows)
+    pool = H.GpuPool(w)
+    sh = H.run_attention(pool, w.seq[perm], w.pos[perm], dev(w.q[perm]), dev(w.k_new[perm]), dev(w.v_new[perm]),
+                         wl.F32, distinct=True).cpu()
+    assert torch.equal(sh, outs[0][torch.as_tensor(perm)])
+
+
 def test_attention_batch_invariance(H):
     """A row gives the same bits alone, in the full batch, in a shuffled batch,
     in a subset, and on a repeated run; chunked and direct pools each."""

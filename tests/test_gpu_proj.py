@@ -82,6 +82,10 @@ GEMV_CASES = [
     (wl.F32, wl.F32, 256, 256, 37, False, True, wl.F32),
     (wl.FP8, wl.BF16, 300, 3584, 2, False, False, wl.F32),
     (wl.FP8, wl.F32, 2 * 64, 1024, 9, True, False, wl.BF16),
+    # enough row groups (>= 8192) that K is not split across a block's waves
+    (wl.BF16, wl.BF16, 33000, 256, 3, False, True, wl.F32),
+    (wl.BF16, wl.BF16, 2 * 16400, 256, 16, True, False, wl.BF16),
+    (wl.FP8, wl.BF16, 32768, 256, 5, False, False, wl.F32),
 ]
 
 
@@ -162,11 +166,13 @@ def test_mfma_tile_height_invariance(H):
         assert torch.equal(part.cpu(), full[r:r + n]), (r, n)
 
 
-@pytest.mark.parametrize("family", [0, 1])
-def test_projection_batch_invariance(H, family):
+@pytest.mark.parametrize("family,rows", [(0, 256), (0, 33000), (1, 256)])
+def test_projection_batch_invariance(H, family, rows):
     """A row's outputs are bit-identical alone, in any batch size (the vector
-    family's register tile changes with the batch) and at any position."""
-    rows, cols = 256, 1024
+    family's register tile changes with the batch) and at any position; for
+    the vector family both with K split over a block's waves (256 rows) and
+    without (33000 rows)."""
+    cols = 1024
     W, s = make_w(rows, cols, wl.BF16, 1)
     x = make_x(300, cols, wl.BF16, 2)
     full, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, family, x, wl.BF16, 300, wl.F32)
