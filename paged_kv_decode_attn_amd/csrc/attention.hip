@@ -269,6 +269,11 @@ struct Acc {
   float l;  // this lane's partial sum of weights
 };
 
+// 2^x by the hardware instruction: results below 2^-126 flush to zero, which
+// no softmax weight or rescale factor here can notice (the running sum is at
+// least 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Online-softmax update of one page from its scores; returns the weights p.
 template <int KVT, int D>
 __device__ __forceinline__ void page_softmax(const AttnParams& P, Acc<KVT, D>& A, const f32x4_t (&S)[2], int pg,
@@ -289,13 +294,13 @@ __device__ __forceinline__ void page_softmax(const AttnParams& P, Acc<KVT, D>& A
   mx = fmaxf(mx, shfl_xor(mx, 16));
   mx = fmaxf(mx, shfl_xor(mx, 32));
   const float m_new = fmaxf(A.m, mx);
-  const float alpha = exp2f(A.m - m_new);
+  const float alpha = fast_exp2(A.m - m_new);
   float ls = 0.f;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[a][i] = exp2f(s[a][i] - m_new);
+      p[a][i] = fast_exp2(s[a][i] - m_new);
       ls += p[a][i];
     }
   A.l = A.l * alpha + ls;
@@ -596,7 +601,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
       for (int j = 0; j < PER; ++j) o[j] = 0.f;
       for (int c = 0; c < nch; ++c) {
         const int64_t rec = ((int64_t)(c0 + c) * P.n_kv + g) * P.G + n;
-        const float w = exp2f(P.part_ml[2 * rec] - M);
+        const float w = fast_exp2(P.part_ml[2 * rec] - M);
         L += P.part_ml[2 * rec + 1] * w;
 #pragma unroll
         for (int j = 0; j < PER; ++j) o[j] += P.part_o[rec * D + PER * l + j] * w;

@@ -21,18 +21,19 @@ constexpr int kPage = 32;
 
 // ------------------------------------------------------------------ formats
 // float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+// f32 -> bf16, round to nearest even, NaN kept quiet, overflow to infinity
+// (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ unsigned f32_to_bf16_bits(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const bf16x2_t v = {(__bf16)f, (__bf16)0.0f};
+  return __builtin_bit_cast(unsigned, v) & 0xffffu;
 }
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned b) { return __uint_as_float(b << 16); }
 // Two bf16 packed in one dword: low half element 0, high half element 1.
 __device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, v);
 }
 
 // Two E4M3 codes (bytes 0/1 of `w` when hi = false, bytes 2/3 when true) -> floats.
