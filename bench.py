@@ -8,8 +8,10 @@ projection, append of each row's key/value, paged attention, output projection
 + residual, gate/up projection + SiLU, down projection + residual.
 
 Prints one JSON line.  `value` = algorithmic HBM bytes of the step / measured
-step time (GB/s); the per-stage breakdown and the dominant kernel's roofline
-are measured with HIP events on the stream the kernels run on.
+step time (GB/s), the step being decode_step captured once in a graph and
+replayed (the eager time is reported beside it); the per-stage breakdown and
+the dominant kernel's roofline are measured with HIP events on the stream the
+kernels run on.
 """
 from __future__ import annotations
 
@@ -173,9 +175,31 @@ def main():
         pkd.decode_step(L, pool.handle, rows, x, y, ws)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_eager = e0.elapsed_time(e1) / args.steps
     pkd.pkd_pool_check(pool.handle)
-    print(f"[bench] decode_step {ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
+    print(f"[bench] decode_step eager {ms_eager * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # The same step captured once in a graph and replayed, as a serving loop
+    # runs it (identical kernels and arguments; only the per-launch host and
+    # queue gaps go).
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(stream)
+    with torch.cuda.stream(gstream):
+        pkd.decode_step(L, pool.handle, rows, x, y, ws, stream=gstream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gstream):
+            pkd.decode_step(L, pool.handle, rows, x, y, ws, stream=gstream)
+        for _ in range(args.warmup):
+            graph.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(gstream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(gstream)
+    torch.cuda.synchronize()
+    ms_step = g0.elapsed_time(g1) / args.steps
+    pkd.pkd_pool_check(pool.handle)
+    print(f"[bench] decode_step graph replay {ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- per stage
     # The same kernels with the same shapes, launched stage by stage through the
@@ -348,6 +372,7 @@ def main():
         "metric": "decode-step us and achieved HBM GB/s (% of peak), paged attn + GEMV",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "us_per_step": round(ms_step * 1e3, 2),
+        "us_per_step_eager": round(ms_eager * 1e3, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.w_dtype], "data": "synthetic",

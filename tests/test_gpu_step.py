@@ -237,3 +237,42 @@ def test_stage_parity(H, orc, name, kw, bar):
     print(f"{name} stage errors: " + ", ".join(f"{k} {v:.2e}" for k, v in e.items()), flush=True)
     for k in ("h", "y"):
         assert e[k] <= bar, k
+
+
+@pytest.mark.parametrize("name,kw,hint", [
+    ("0.6b-mixed-bf16", dict(n_decode=24, chunk_rows=12, chunk=4, long_max=1400), 8),
+    ("7b-b4096-fp8", dict(n=64, L=100), 64),
+])
+def test_step_graph_replay(H, name, kw, hint):
+    """decode_step captured in a graph and replayed several times, with eager
+    work and synchronisation between replays, gives the eager result every
+    time (chunked attention with its plan and merge kernels, K-split
+    projections with their finish kernels, fp8 activation quantisation)."""
+    import paged_kv_decode_attn_amd as pkd
+    w = wl.make(name, "cpu", **kw)
+    layer = H.GpuLayer(w, batch_hint=hint)
+    pool = H.GpuPool(w)
+    s_t, p_t = H.rows_tensors(w.seq, w.pos)
+    rows = pkd.make_rows(s_t, p_t, len(set(w.seq.tolist())) == w.n_rows)
+    n = w.n_rows
+    x = w.x.cuda().contiguous()
+    y = torch.empty((n, w.hidden), dtype=torch.float32, device="cuda")
+    ws = H.aligned_empty(pkd.pkd_step_workspace_bytes(layer.layer, pool.handle, n))
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        pkd.decode_step(layer.layer, pool.handle, rows, x, y, ws, stream=st)
+        torch.cuda.synchronize()
+        eager = y.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            pkd.decode_step(layer.layer, pool.handle, rows, x, y, ws, stream=st)
+    torch.cuda.synchronize()
+    scratch = torch.randn((1 << 20,), device="cuda")
+    for rep in range(4):
+        y.fill_(float("nan"))
+        scratch.mul_(1.0001)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), rep
+    pkd.pkd_pool_check(pool.handle)
