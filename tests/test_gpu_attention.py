@@ -205,6 +205,42 @@ def test_invalid_rows_zeroed_and_reported(H):
         pkd.pkd_pool_check(pool.handle)  # cleared
 
 
+def test_invalid_rows_fused_append_and_flag_refusal(H):
+    """Rows with a bad sequence or position are zeroed and reported on the
+    fused-append path too (and append nothing); unknown row flags are refused
+    before anything runs."""
+    import paged_kv_decode_attn_amd as pkd
+    w = wl.make("attn", "cpu", seed=9, n_q=4, n_kv=2, d=128, kv_dtype=wl.BF16, lens=(20, 40), append=True,
+                chunk=8, extra_pages=0)
+    pool = H.GpuPool(w)
+    before = pool.pages_bytes().clone()
+    seq = np.asarray([0, 5, -1], np.int32)
+    pos = np.asarray([19, 3, 0], np.int32)
+    q = torch.cat([w.q] * 2)[:3].cuda()
+    kn = torch.cat([w.k_new] * 2)[:3].cuda()
+    vn = torch.cat([w.v_new] * 2)[:3].cuda()
+    out = H.run_attention(pool, seq, pos, q, kn, vn, distinct=True).cpu()
+    assert torch.equal(out[1], torch.zeros_like(out[1])) and torch.equal(out[2], torch.zeros_like(out[2]))
+    assert out[0].abs().sum() > 0
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.pkd_pool_check(pool.handle)
+    assert ei.value.status == 7
+    # only sequence 0's page 0 (its token 19) changed
+    after = pool.pages_bytes()
+    changed = torch.nonzero(after != before).flatten()
+    blk = pool.info.block_bytes
+    page0 = int(w.tables[0][0])
+    assert changed.numel() > 0
+    assert bool(((changed // (2 * 2 * blk)) == page0).all())
+    s_t, p_t = H.rows_tensors(seq, pos)
+    rows = pkd.pkd_rows(s_t.data_ptr(), p_t.data_ptr(), 3, 2)
+    o2 = torch.empty_like(out).cuda()
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.paged_attn_decode(pool.handle, rows, 4, q, kn, vn, o2, 0,
+                              H.aligned_empty(pkd.pkd_attn_workspace_bytes(pool.handle, 4, 3)))
+    assert ei.value.status == 1
+
+
 def test_block_table_refusals(H):
     import paged_kv_decode_attn_amd as pkd
     w = wl.make("attn", "cpu", seed=8, n_q=4, n_kv=2, d=64, kv_dtype=wl.F32, lens=(20, 40), append=False,
