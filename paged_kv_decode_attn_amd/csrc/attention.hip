@@ -317,6 +317,29 @@ __device__ __forceinline__ void load_block(const uint8_t* b, PageRegs<KVT, D>& r
   for (int j = 0; j < GE::NL; ++j) r[j] = load16(k + 1024 * j);
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// The same block from its staged copy in LDS (identical byte layout).
+template <int KVT, int D>
+__device__ __forceinline__ void load_block_lds(const lds_u8* b, PageRegs<KVT, D>& r) {
+  using GE = Geo<KVT, D>;
+  const lds_u8* k = b + 16 * lane_id();
+#pragma unroll
+  for (int j = 0; j < GE::NL; ++j) r[j] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(k + 1024 * j);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (lds wave-uniform).  The host compilation pass never sees the
+// device builtin.
+__device__ __forceinline__ void dma16(const uint8_t* g, lds_u8* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#else
+  (void)g;
+  (void)lds;
+#endif
+}
+
 // Row r's own key and value for kv head g, as the pool stores them: lane l
 // holds dims l and l + 64 (and so on) of each, already converted to the pool
 // dtype (bits in the low bytes).  Loaded early; stored by append_store.
@@ -378,9 +401,14 @@ __device__ __forceinline__ void append_store(const AttnParams& P, int g, int pag
 // consumed the current K, and its V once the P.V products have consumed the
 // current V, so a wave keeps about one page in flight with half the registers
 // of a double buffer and three waves fit on a SIMD.
+// staged / n_staged: logical pages [0, n_staged) of the row are shared with the
+// other rows of the workgroup and were staged in LDS once for all of them
+// (page j's K block at staged + 2 j block_bytes, its V block after it); they
+// are read from there, byte for byte what the global loads would return.
 template <int KVT, int D, bool FUSE = false>
 __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, int r, int s, int p_row, int g,
-                                         int pg0, int pg1, int tab) {
+                                         int pg0, int pg1, int tab, const lds_u8* staged = nullptr,
+                                         int n_staged = 0) {
   using GE = Geo<KVT, D>;
   u32x4 qv[GE::NQ];
   float qf[GE::NQ];
@@ -410,26 +438,30 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
   NewToken<KVT, D> nt;
   if constexpr (FUSE) append_load<KVT, D>(P, r, g, nt);
   u32x4 kr[GE::NL], vr[GE::NL];
-  const uint8_t* cur = base + (uint64_t)page_of(pg0) * P.page_stride;
+  // K (c = 0) or V (c = 1) block of logical page pg, from LDS when staged
+  auto load = [&](int pg, int c, PageRegs<KVT, D>& regs) {
+    if (pg < n_staged) load_block_lds<KVT, D>(staged + (2 * pg + c) * P.block_bytes, regs);
+    else load_block<KVT, D>(base + (uint64_t)page_of(pg) * P.page_stride + c * P.block_bytes, regs);
+  };
   if (FUSE && own == pg0) {
     append_store<KVT, D>(P, g, page_of(own), p_row % kPage, nt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  load_block<KVT, D>(cur, kr);
-  load_block<KVT, D>(cur + P.block_bytes, vr);
+  load(pg0, 0, kr);
+  load(pg0, 1, vr);
   if (FUSE && own != pg0) append_store<KVT, D>(P, g, page_of(own), p_row % kPage, nt);
   for (int pg = pg0; pg < pg1; ++pg) {
-    const uint8_t* nxt = pg + 1 < pg1 ? base + (uint64_t)page_of(pg + 1) * P.page_stride : nullptr;
+    const bool nxt = pg + 1 < pg1;
     f32x4_t S[2];
     page_scores<KVT, D>(kr, qv, qf, S);
     if (FUSE && pg + 1 == own) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (nxt) load_block<KVT, D>(nxt, kr);
+    if (nxt) load(pg + 1, 0, kr);
     bool valid[2][4];
     float p[2][4];
     page_softmax<KVT, D>(P, A, S, pg, p_row, valid, p);
     if ((pg + 1) * kPage > p_row + 1) mask_v<KVT, D>(vr, valid);  // partial last page
     page_pv<KVT, D>(vr, p, A.O);
-    if (nxt) load_block<KVT, D>(nxt + P.block_bytes, vr);
+    if (nxt) load(pg + 1, 1, vr);
   }
 }
 
@@ -477,18 +509,76 @@ __device__ __forceinline__ void zero_heads(const AttnParams& P, int r, int g) {
 // One wave per (row, kv head); every row is a single chunk.
 //   FUSE: every sequence has one row in the launch; the wave also appends its
 //   row's token (see run_unit).
+// A workgroup holds four consecutive rows (one wave each) for one kv head.
+// Leading logical pages that every valid row of the workgroup maps to the same
+// physical page (a shared prompt prefix), other than any row's last page (the
+// page its own token goes to), are loaded into LDS once and read from there by
+// all four waves.
+template <int KVT, int D>
+struct Stage {
+  static constexpr int BLOCK = kPage * D * Geo<KVT, D>::ES;  // bytes of one K or V block
+  static constexpr int PAGES = (32768 / (2 * BLOCK)) < 4 ? (32768 / (2 * BLOCK)) : 4;
+  static constexpr int BYTES = PAGES * 2 * BLOCK;            // at most 32 KiB
+};
+
 template <int KVT, int D, bool FUSE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attn_direct_kernel(AttnParams P) {
-  const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
-  const int s = P.seq[r], p = P.pos[r];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_direct_kernel(AttnParams P) {
+  using ST = Stage<KVT, D>;
+  __shared__ __attribute__((aligned(16))) uint8_t stage_mem[ST::BYTES];
+  __shared__ int meta[4][2 + ST::PAGES];  // per wave: valid, page count, first table entries
+  const int wave = threadIdx.x >> 6, l = lane_id();
+  const int r = blockIdx.x * 4 + wave, g = blockIdx.y;
+  const bool in_range = r < P.n_rows;
+  const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
   int count, tab;
   row_meta(P, s, count, tab);
-  if (!row_ok(P, s, p, count, g == 0)) {
+  const bool ok = in_range && row_ok(P, s, p, count, g == 0);
+  if (l < ST::PAGES) meta[wave][2 + l] = tab;
+  if (l == 0) {
+    meta[wave][0] = ok ? 1 : 0;
+    meta[wave][1] = ok ? (p + kPage) / kPage : 0;
+  }
+  __syncthreads();
+  // pages every valid row shares (same for all four waves)
+  int n_valid = 0, lead = -1, n_staged = ST::PAGES;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (!meta[w][0]) continue;
+    ++n_valid;
+    if (lead < 0) lead = w;
+    n_staged = min(n_staged, meta[w][1] - 1);  // never a row's last page
+  }
+  if (n_valid < 2) n_staged = 0;
+  for (int j = 0; j < n_staged; ++j) {
+    bool same = true;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (meta[w][0] && meta[w][2 + j] != meta[lead][2 + j]) same = false;
+    if (!same) {
+      n_staged = j;
+      break;
+    }
+  }
+  lds_u8* staged = (lds_u8*)stage_mem;
+  if (n_staged > 0) {
+    // 1 KiB wave loads: page j, block c, part i; dealt round-robin to the waves
+    constexpr int PARTS = ST::BLOCK / 1024;
+    const uint8_t* gbase = P.pages + (uint64_t)g * 2 * P.block_bytes;
+    for (int q = wave; q < n_staged * 2 * PARTS; q += 4) {
+      const int j = q / (2 * PARTS), c = (q / PARTS) % 2, i = q % PARTS;
+      const uint8_t* src = gbase + (uint64_t)meta[lead][2 + j] * P.page_stride + c * P.block_bytes + 1024 * i + 16 * l;
+      dma16(src, staged + (2 * j + c) * ST::BLOCK + 1024 * i);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (!in_range) return;
+  if (!ok) {
     zero_heads<D>(P, r, g);
     return;
   }
   Acc<KVT, D> A;
-  run_unit<KVT, D, FUSE>(P, A, r, s, p, g, 0, (p + kPage) / kPage, tab);
+  run_unit<KVT, D, FUSE>(P, A, r, s, p, g, 0, (p + kPage) / kPage, tab, staged, n_staged);
   finish<KVT, D>(P, A, r, g);
 }
 
@@ -688,13 +778,14 @@ template <int KVT, int D>
 static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk,
                        hipStream_t st) {
   const int units = a.n_rows * n_kv;
+  const dim3 tiles((a.n_rows + 3) / 4, n_kv);  // direct mode: four rows of one kv head per workgroup
   if (!chunk && a.k_new && a.distinct) {
-    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true>), dim3(units), dim3(64), 0, st, P);
+    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true>), tiles, dim3(256), 0, st, P);
     return;
   }
   if (a.k_new) hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
   if (!chunk) {
-    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false>), dim3(units), dim3(64), 0, st, P);
+    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false>), tiles, dim3(256), 0, st, P);
     return;
   }
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, st, P, w.row_chunks);

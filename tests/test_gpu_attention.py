@@ -113,6 +113,30 @@ def test_fused_append_bit_identical(H, kvt, nq, nkv, d):
     assert torch.equal(sh, outs[0][torch.as_tensor(perm)])
 
 
+@pytest.mark.parametrize("kvt,nq,nkv,d,append", [
+    (wl.BF16, 14, 2, 128, True), (wl.BF16, 4, 2, 128, False), (wl.FP8, 14, 2, 128, True),
+    (wl.F32, 4, 2, 64, True), (wl.BF16, 32, 2, 64, False)])
+def test_shared_prefix_staging(H, orc, kvt, nq, nkv, d, append):
+    """Rows whose first page is one physical page: in a batch, each workgroup
+    of four rows stages that page in LDS once; alone, a row reads it from HBM.
+    The bits agree, and both match the oracle."""
+    lens = (40, 50, 70, 100, 33, 64, 65, 129, 97)
+    w = wl.make("attn", "cpu", seed=21 + nq + d + kvt, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens,
+                append=append, chunk=8, shared_first_page=True)
+    assert all(int(w.tables[s][0]) == int(w.tables[0][0]) for s in range(len(lens)))
+    dev = lambda t: None if t is None else t.to("cuda")
+    full = H.run_attention(H.GpuPool(w), w.seq, w.pos, dev(w.q), dev(w.k_new), dev(w.v_new), wl.F32,
+                           distinct=True).cpu()
+    want = oracle_attn(orc, w, w.seq, w.pos, w.q, w.k_new, w.v_new)
+    assert H.rel_err(full.numpy().astype(np.float64), want) <= TOL_F32_OUT
+    for r in range(len(lens)):
+        sl = slice(r, r + 1)
+        one = H.run_attention(H.GpuPool(w), w.seq[sl], w.pos[sl], dev(w.q[sl]),
+                              None if w.k_new is None else dev(w.k_new[sl]),
+                              None if w.v_new is None else dev(w.v_new[sl]), wl.F32, distinct=True).cpu()
+        assert torch.equal(one[0], full[r]), r
+
+
 def test_attention_batch_invariance(H):
     """A row gives the same bits alone, in the full batch, in a shuffled batch,
     in a subset, and on a repeated run; chunked and direct pools each."""
