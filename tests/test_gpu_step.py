@@ -276,3 +276,34 @@ def test_step_graph_replay(H, name, kw, hint):
         torch.cuda.synchronize()
         assert torch.equal(y, eager), rep
     pkd.pkd_pool_check(pool.handle)
+
+
+def test_zero_rows_are_no_ops(H):
+    """n = 0 is a valid call for every entry point: it returns OK, launches
+    nothing and leaves outputs and the pool untouched."""
+    import paged_kv_decode_attn_amd as pkd
+    w = wl.make("tiny-f32", "cpu")
+    pool = H.GpuPool(w)
+    layer = H.GpuLayer(w)
+    before = pool.pages_bytes().clone()
+    s_t = torch.zeros(0, dtype=torch.int32, device="cuda")
+    rows = pkd.make_rows(s_t, s_t)
+    y = torch.full((1, w.hidden), 7.0, device="cuda")
+    x = torch.ones((1, w.hidden), device="cuda")
+    ws = H.aligned_empty(max(pkd.pkd_step_workspace_bytes(layer.layer, pool.handle, 1), 256))
+    pkd.decode_step(layer.layer, pool.handle, rows, x, y, ws)
+    out = torch.full((1, w.n_q, w.head_dim), 7.0, device="cuda")
+    q = torch.ones((1, w.n_q, w.head_dim), device="cuda")
+    pkd.paged_attn_decode(pool.handle, rows, w.n_q, q, q[:, :w.n_kv].contiguous(), q[:, :w.n_kv].contiguous(),
+                          out, wl.F32, ws)
+    for wdt, fam in ((wl.F32, 0), (wl.BF16, 1)):
+        W = wl.encode(torch.ones((256, 256)), wdt).cuda()
+        M = pkd.make_matrix(W, 256, 256, wdt, 1.0, fam)
+        xin = wl.encode(torch.ones((1, 256)), wdt).cuda()
+        yy = torch.full((1, 256), 7.0, device="cuda")
+        pkd.gemv_rows(M, xin, wdt, 0, yy, wl.F32)
+        assert bool((yy == 7.0).all())
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all()) and bool((out == 7.0).all())
+    assert torch.equal(pool.pages_bytes(), before)
+    pkd.pkd_pool_check(pool.handle)
