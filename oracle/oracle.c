@@ -204,6 +204,35 @@ void orc_matvec_rows(int dtype, const void* W, double scale, int rows, int cols,
   }
 }
 
+/* Logits for a per-row candidate list only ("GPU inference engine
+ * engineering": headline figure "Grammar-bounded output" and section "The
+ * whole decode loop on the GPU": the output layer is evaluated for the rows
+ * that can be emitted next, not for the whole vocabulary).  For r < n and
+ * c < clamp(n_cand[r], 0, max_cand): j = cand[r][c];
+ *   Y[r][c] = sum_k (W[j][k] * scale) * X[r][k]   if 0 <= j < rows,
+ *   Y[r][c] = NaN                                  otherwise.
+ * Entries at c >= the clamped count are left as the caller filled them. */
+void orc_matvec_gathered(int dtype, const void* W, double scale, int rows, int cols,
+                         const double* X, int n, const int32_t* cand, int max_cand,
+                         const int32_t* n_cand, double* Y) {
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < n; ++r) {
+    int cnt = n_cand[r];
+    if (cnt < 0) cnt = 0;
+    if (cnt > max_cand) cnt = max_cand;
+    for (int c = 0; c < cnt; ++c) {
+      int j = cand[(int64_t)r * max_cand + c];
+      double acc = NAN;
+      if (j >= 0 && j < rows) {
+        acc = 0.0;
+        for (int k = 0; k < cols; ++k)
+          acc += code_value(W, dtype, (int64_t)j * cols + k) * scale * X[(int64_t)r * cols + k];
+      }
+      Y[(int64_t)r * max_cand + c] = acc;
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Pool layout (read side), written from the documented layout of the ABI    */
 /* ------------------------------------------------------------------------ */

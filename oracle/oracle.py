@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
         L.orc_matvec_rows.argtypes = [ctypes.c_int, P, ctypes.c_double, ctypes.c_int,
                                       ctypes.c_int, P, ctypes.c_int, P]
         L.orc_matvec_rows.restype = None
+        L.orc_matvec_gathered.argtypes = [ctypes.c_int, P, ctypes.c_double, ctypes.c_int, ctypes.c_int, P,
+                                          ctypes.c_int, P, ctypes.c_int, P, P]
+        L.orc_matvec_gathered.restype = None
         L.orc_gather_history.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P,
                                          ctypes.c_int, ctypes.c_int, P, P]
         L.orc_gather_history.restype = ctypes.c_int
@@ -136,6 +139,25 @@ def matvec_rows(dtype: int, W: np.ndarray, scale: float, X: np.ndarray) -> np.nd
     X2 = X.reshape(-1, cols)
     Y = np.empty((X2.shape[0], rows), np.float64)
     lib().orc_matvec_rows(dtype, _ptr(W), float(scale), rows, cols, _ptr(X2), X2.shape[0], _ptr(Y))
+    return Y
+
+
+def matvec_gathered(dtype: int, W: np.ndarray, scale: float, X: np.ndarray, cand: np.ndarray,
+                    n_cand: np.ndarray, fill: float = 0.0) -> np.ndarray:
+    """Y[r][c] = sum_k W[cand[r][c]][k] * scale * X[r][k] in fp64 for
+    c < clamp(n_cand[r], 0, max_cand); NaN for an index outside the matrix;
+    `fill` elsewhere."""
+    W = _c(W, _NP[dtype])
+    X = _c(X, np.float64)
+    rows, cols = W.shape
+    X2 = X.reshape(-1, cols)
+    cand = _c(cand, np.int32)
+    n = X2.shape[0]
+    cand = cand.reshape(n, -1)
+    n_cand = _c(n_cand, np.int32)
+    Y = np.full((n, cand.shape[1]), fill, np.float64)
+    lib().orc_matvec_gathered(dtype, _ptr(W), float(scale), rows, cols, _ptr(X2), n, _ptr(cand),
+                              cand.shape[1], _ptr(n_cand), _ptr(Y))
     return Y
 
 

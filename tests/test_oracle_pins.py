@@ -127,8 +127,7 @@ def test_matvec_closed_forms(orc):
     cols = 512
     X = rng.standard_normal((3, cols))
     eye = np.eye(cols, dtype=np.float32)
-    assert np.array_equal(orc.matvec_rows(orc.F32, eye, 1.0, X), X.astype(np.float32).astype(np.float64)
-                          if False else X)
+    assert np.array_equal(orc.matvec_rows(orc.F32, eye, 1.0, X), X)
     onehot = np.zeros((4, cols), np.float32)
     idx = [7, 0, 511, 100]
     onehot[np.arange(4), idx] = 1.0
@@ -152,6 +151,50 @@ def test_matvec_vs_numpy_all_dtypes(orc):
         assert np.allclose(got, want, rtol=1e-12, atol=1e-14), dt
         # linearity in x is exact up to fp64 rounding
         assert np.allclose(orc.matvec_rows(dt, codes, s, 2.0 * X), 2.0 * got, rtol=0, atol=0)
+
+
+def test_matvec_gathered_closed_forms(orc):
+    """Identity rows pick the activation entries the candidate list names, in
+    the list's order; a bad index gives NaN; entries past the (clamped) count
+    keep the caller's fill; a repeated index gives the same value twice."""
+    rng = np.random.default_rng(11)
+    cols = 256
+    X = rng.standard_normal((4, cols))
+    eye = np.eye(cols, dtype=np.float32)
+    cand = np.array([[5, 0, 255, 5, 9, 9],
+                     [255, 254, 1, 0, 0, 0],
+                     [3, -1, cols, 7, 0, 0],
+                     [11, 12, 13, 14, 15, 16]], np.int32)
+    n_cand = np.array([6, 3, 4, 99], np.int32)
+    Y = orc.matvec_gathered(orc.F32, eye, 1.0, X, cand, n_cand, fill=-7.0)
+    assert np.array_equal(Y[0], X[0, [5, 0, 255, 5, 9, 9]])
+    assert np.array_equal(Y[1, :3], X[1, [255, 254, 1]]) and (Y[1, 3:] == -7.0).all()
+    assert Y[2, 0] == X[2, 3] and np.isnan(Y[2, 1]) and np.isnan(Y[2, 2]) and Y[2, 3] == X[2, 7]
+    assert (Y[2, 4:] == -7.0).all()
+    assert np.array_equal(Y[3], X[3, 11:17])  # a count above max_cand is clamped
+    Y0 = orc.matvec_gathered(orc.F32, eye, 1.0, X, cand, np.array([0, -3, 0, 0], np.int32), fill=2.5)
+    assert (Y0 == 2.5).all()
+
+
+def test_matvec_gathered_vs_numpy_all_dtypes(orc):
+    """Each gathered entry is the product of that weight row with that
+    activation row (numpy over the decoded weights), for every storage dtype
+    and with a per-tensor scale."""
+    rng = np.random.default_rng(12)
+    W = torch.from_numpy(rng.standard_normal((300, 128)).astype(np.float32) * 0.05)
+    X = rng.standard_normal((6, 128))
+    cand = rng.integers(0, 300, size=(6, 28)).astype(np.int32)
+    n_cand = np.array([28, 1, 0, 17, 28, 5], np.int32)
+    for dt in (orc.F32, orc.BF16, orc.FP8):
+        s = wl.fp8_scale(W) if dt == orc.FP8 else 1.0
+        codes = wl.to_numpy_codes(wl.encode(W, dt, s), dt)
+        Wv = orc.code_values(codes, dt, s)
+        got = orc.matvec_gathered(dt, codes, s, X, cand, n_cand, fill=np.nan)
+        for r in range(6):
+            k = n_cand[r]
+            want = Wv[cand[r, :k]] @ X[r]
+            assert np.allclose(got[r, :k], want, rtol=1e-12, atol=1e-14), (dt, r)
+            assert np.isnan(got[r, k:]).all()
 
 
 # ----------------------------------------------------------------------------- attention
