@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--workload", default="7b-b768-prefix-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-t2", action="store_true", help="skip the small-batch GEMV pass")
+    ap.add_argument("--no-head", action="store_true", help="skip the output-head (candidate rows) pass")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--family", type=int, default=None, help="override the projection family")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -345,6 +346,45 @@ def main():
             byt = wbytes + nb * 2 * (D + nq * d + D + F) + nb * (2 * nqkv + 8 * D + 2 * F + 8 * D)
             t2_res[f"B{nb}"] = {"us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2), "bytes": int(byt),
                             "GB_s": round(byt / med / 1e3, 1), "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4)}
+    # Output head over a tied embedding (151,936 x 2,048 bf16, 593.5 MiB): the
+    # dense head at batch 1 against the candidate-row head, whose rows carry
+    # trie-shaped lists of 1..28 candidates, cold.
+    head_res = None
+    if not args.no_head:
+        V, HD, HC = wl.HEAD_VOCAB, wl.HEAD_HIDDEN, wl.HEAD_MAX_CAND
+        gh = torch.Generator(device="cuda").manual_seed(7)
+        Wh = torch.empty((V, HD), dtype=torch.int16, device="cuda")
+        for i in range(0, V, 16384):
+            blk = torch.randn((min(16384, V - i), HD), generator=gh, device="cuda") * 0.02
+            Wh[i:i + blk.shape[0]] = blk.to(torch.bfloat16).view(torch.int16)
+        Mh = pkd.make_matrix(Wh, V, HD, 1, 1.0, 0)
+        head_res = {"vocab": V, "hidden": HD, "max_cand": HC, "dtype": "bf16", "matrix_bytes": V * HD * 2}
+        for nb in (1, 64, 512):
+            xh = (torch.randn((nb, HD), generator=gh, device="cuda")).to(torch.bfloat16).view(torch.int16)
+            cand, n_cand = wl.head_candidates(nb, V, HC, 1000 + nb)
+            cd, nd = torch.from_numpy(cand).cuda(), torch.from_numpy(n_cand).cuda()
+            yh = torch.empty((nb, HC), device="cuda")
+            gbytes = int(n_cand.sum()) * HD * 2 + nb * HD * 2 + int(n_cand.sum()) * 4 + nb * HC * 4 + nb * 4
+            for _ in range(3):
+                pkd.gemv_gather_rows(Mh, xh, 1, nb, cd, nd, HC, yh)
+            med, p10, p90 = timed(lambda: pkd.gemv_gather_rows(Mh, xh, 1, nb, cd, nd, HC, yh),
+                                  max(args.steps, 10), True)
+            ent = {"gathered_us": round(med, 2), "gathered_p10_us": round(p10, 2), "gathered_p90_us": round(p90, 2),
+                   "gathered_bytes": gbytes, "gathered_GB_s": round(gbytes / med / 1e3, 1),
+                   "mean_candidates": round(float(n_cand.mean()), 2)}
+            if nb == 1:
+                yd = torch.empty((nb, V), device="cuda")
+                for _ in range(3):
+                    pkd.gemv_rows(Mh, xh, 1, nb, yd, 0)
+                dmed, _, _ = timed(lambda: pkd.gemv_rows(Mh, xh, 1, nb, yd, 0), max(args.steps, 10), True)
+                dbytes = V * HD * 2 + HD * 2 + V * 4
+                ent.update({"dense_us": round(dmed, 2), "dense_bytes": dbytes,
+                            "dense_GB_s": round(dbytes / dmed / 1e3, 1),
+                            "dense_hbm_frac": round(dbytes / dmed / 1e3 / HBM_PEAK_GBS, 4),
+                            "speedup_vs_dense": round(dmed / med, 1)})
+                del yd
+            head_res[f"B{nb}"] = ent
+        del Wh, Mh
     del flush, flush_sum
 
     # ---------------------------------------------------------------- CPU baseline
@@ -384,6 +424,7 @@ def main():
         "roofline": roofline,
         "t1_attention": t1_res,
         "t2_gemv": t2_res,
+        "output_head": head_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -333,6 +333,36 @@ pkd_status gemv_rows(const pkd_matrix* W, const void* x, int32_t x_dtype, int32_
                      void* y, const pkd_epilogue* ep, void* ws, size_t ws_bytes,
                      pkd_stream stream, pkd_error* err);
 
+/*
+ * Logits for a candidate list of weight rows only: the output head evaluated
+ * for the tokens that may come next rather than for the whole vocabulary
+ * ("GPU inference engine engineering", headline figure "Grammar-bounded
+ * output" and section "The whole decode loop on the GPU").
+ *
+ * For each activation row r < n_rows of x (device [n_rows][W->cols], f32 or
+ * bf16 per x_dtype) and each c < clamp(n_cand[r], 0, max_cand):
+ *   j = cand[r * max_cand + c];
+ *   y[r * max_cand + c] = W->scale * sum_k W[j][k] x[r][k]   (0 <= j < rows)
+ *                       = NaN                                 (otherwise)
+ * Entries y[r][c] at c >= that clamped count are not written.
+ *   cand:   device int32 [n_rows][max_cand], weight-row indices; repeats allowed.
+ *   n_cand: device int32 [n_rows], entries used per row.
+ *   y:      device f32 [n_rows][max_cand].
+ * W must be a GEMV-family matrix (any storage dtype).  Each y entry is
+ * bit-identical to the same entry of gemv_rows(W, x) with an f32 output,
+ * whatever the batch, list length or order (same K split, same summation
+ * order), so the full head can serve as a cross-check of the gathered one.
+ * Bytes read: sum_r clamp(n_cand[r]) rows of W plus x; no workspace.
+ * Errors (host-side, before any launch): NULL/misaligned pointers
+ * (x and y 16-byte, cand/n_cand 4-byte), max_cand < 1 when n_rows > 0 ->
+ * PKD_ERR_INVALID_ARG; a matrix-core family or n_rows > 65535 ->
+ * PKD_ERR_UNSUPPORTED.  Asynchronous on `stream`; the caller owns every
+ * buffer.
+ */
+pkd_status gemv_gather_rows(const pkd_matrix* W, const void* x, int32_t x_dtype, int32_t n_rows,
+                            const int32_t* cand, const int32_t* n_cand, int32_t max_cand, float* y,
+                            pkd_stream stream, pkd_error* err);
+
 /* ------------------------------------------------------------------------ */
 /* One decode step of one transformer layer                                  */
 /* ------------------------------------------------------------------------ */

@@ -79,7 +79,7 @@ class pkd_layer(ctypes.Structure):
 
 EXPORTS = ["pkd_pool_bytes", "kv_pool_create", "kv_pool_destroy", "pkd_pool_info_get", "block_table_set",
            "pkd_pool_check", "pkd_attn_workspace_bytes", "paged_attn_decode", "pkd_gemv_workspace_bytes",
-           "pkd_suggest_k_splits", "gemv_rows", "pkd_step_workspace_bytes", "decode_step", "pkd_status_string", "pkd_version"]
+           "pkd_suggest_k_splits", "gemv_rows", "gemv_gather_rows", "pkd_step_workspace_bytes", "decode_step", "pkd_status_string", "pkd_version"]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -102,6 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkd_suggest_k_splits": (I32, [I32, I32, I32, I32]),
         "gemv_rows": (I32, [ctypes.POINTER(pkd_matrix), P, I32, I32, P, ctypes.POINTER(pkd_epilogue), P, SZ,
                             P, E]),
+        "gemv_gather_rows": (I32, [ctypes.POINTER(pkd_matrix), P, I32, I32, P, P, I32, P, P, E]),
         "pkd_step_workspace_bytes": (SZ, [ctypes.POINTER(pkd_layer), P, I32]),
         "decode_step": (I32, [ctypes.POINTER(pkd_layer), P, ctypes.POINTER(pkd_rows), P, P, P, SZ, P, E]),
         "pkd_status_string": (ctypes.c_char_p, [I32]),
@@ -184,7 +185,9 @@ def pkd_pool_check(pool, stream=None) -> None:
 
 # ------------------------------------------------------------------ attention
 def make_rows(seq: torch.Tensor, pos: torch.Tensor, distinct: bool = False) -> pkd_rows:
-    return pkd_rows(_ptr(seq), _ptr(pos), int(seq.numel()), ROWS_DISTINCT_SEQS if distinct else 0)
+    r = pkd_rows(_ptr(seq), _ptr(pos), int(seq.numel()), ROWS_DISTINCT_SEQS if distinct else 0)
+    r._keep = (seq, pos)  # the struct holds raw pointers: keep the tensors alive with it
+    return r
 
 
 def pkd_attn_workspace_bytes(pool, n_q_heads: int, max_rows: int) -> int:
@@ -203,7 +206,9 @@ def paged_attn_decode(pool, rows: pkd_rows, n_q_heads: int, q, k_new, v_new, out
 # ------------------------------------------------------------------ projections
 def make_matrix(data: torch.Tensor, rows: int, cols: int, dtype: int, scale: float = 1.0,
                 family: int = FAMILY_GEMV, k_splits: int = 1) -> pkd_matrix:
-    return pkd_matrix(_ptr(data), rows, cols, dtype, scale, family, k_splits)
+    m = pkd_matrix(_ptr(data), rows, cols, dtype, scale, family, k_splits)
+    m._keep = data  # the struct holds a raw pointer: keep the tensor alive with it
+    return m
 
 
 def pkd_gemv_workspace_bytes(W: pkd_matrix, max_rows: int) -> int:
@@ -221,6 +226,14 @@ def gemv_rows(W: pkd_matrix, x, x_dtype: int, n_rows: int, y, out_dtype: int = F
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gemv_rows(ctypes.byref(W), _ptr(x), x_dtype, n_rows, _ptr(y), ctypes.byref(ep), _ptr(ws),
                            ws_bytes, _stream(stream), ctypes.byref(err)), err)
+
+
+def gemv_gather_rows(W: pkd_matrix, x, x_dtype: int, n_rows: int, cand, n_cand, max_cand: int, y,
+                     stream=None) -> None:
+    """y[r][c] = W[cand[r][c]] . x[r] for c < n_cand[r] (f32 logits)."""
+    err = pkd_error()
+    _check(lib().gemv_gather_rows(ctypes.byref(W), _ptr(x), x_dtype, n_rows, _ptr(cand), _ptr(n_cand), max_cand,
+                                  _ptr(y), _stream(stream), ctypes.byref(err)), err)
 
 
 # ------------------------------------------------------------------ decode step

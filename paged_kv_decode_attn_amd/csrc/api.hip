@@ -360,6 +360,30 @@ pkd_status gemv_rows(const pkd_matrix* W, const void* x, int32_t x_dtype, int32_
   return proj_launch(a, ws, ws_bytes, (hipStream_t)stream, err);
 }
 
+pkd_status gemv_gather_rows(const pkd_matrix* W, const void* x, int32_t x_dtype, int32_t n_rows,
+                            const int32_t* cand, const int32_t* n_cand, int32_t max_cand, float* y,
+                            pkd_stream stream, pkd_error* err) {
+  ProjArgs a{};
+  a.W = W;
+  a.x = x;
+  a.x_dtype = x_dtype;
+  a.n_rows = n_rows;
+  a.y = y;
+  a.out_dtype = PKD_F32;
+  pkd_status s = proj_validate(a, err);
+  if (s != PKD_OK) return s;
+  if (W->family != PKD_FAMILY_GEMV)
+    return fail(err, PKD_ERR_UNSUPPORTED, W->family, PKD_FAMILY_GEMV,
+                "gathered rows are evaluated with the vector family's summation order only");
+  if (n_rows > 65535) return fail(err, PKD_ERR_UNSUPPORTED, n_rows, 65535, "at most 65535 activation rows");
+  if (n_rows == 0) return PKD_OK;
+  if (max_cand < 1) return fail(err, PKD_ERR_INVALID_ARG, max_cand, 1, "max_cand must be positive");
+  if (!cand || !n_cand) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "cand or n_cand is NULL");
+  if (((uintptr_t)cand | (uintptr_t)n_cand) & 3)
+    return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "cand and n_cand must be 4-byte aligned");
+  return gemv_gather_launch(*W, x, x_dtype, n_rows, cand, n_cand, max_cand, y, (hipStream_t)stream, err);
+}
+
 // ------------------------------------------------------------------ decode step
 struct StepWs {
   void* x_in;   // [n][D] bf16 (bf16 tier)

@@ -132,6 +132,9 @@ size_t proj_workspace_bytes(const pkd_matrix* W, int32_t max_rows);
 int suggest_k_splits(int rows, int cols, int family, int typical_rows);
 pkd_status proj_validate(const ProjArgs& a, pkd_error* err);
 pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err);
+pkd_status gemv_gather_launch(const pkd_matrix& W, const void* x, int32_t x_dtype, int32_t n_rows,
+                              const int32_t* cand, const int32_t* n_cand, int32_t max_cand, float* y,
+                              hipStream_t stream, pkd_error* err);
 
 // Elementwise f32 -> bf16 rounding of n values (projection inputs).
 pkd_status cast_bf16_launch(const float* x, void* y, int64_t n, hipStream_t stream, pkd_error* err);

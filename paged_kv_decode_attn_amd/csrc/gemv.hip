@@ -37,6 +37,11 @@ struct GemvParams {
   const float* residual;
   uint16_t* y2;  // optional bf16 copy
   int32_t n_out;  // outputs per activation row (rows, or rows / 2 with silu)
+  // Gathered rows: activation row r evaluates only the weight rows
+  // cand[r][0 .. n_cand[r]) (y is then [n_rows][max_cand] f32).
+  const int32_t* cand;
+  const int32_t* n_cand;
+  int32_t max_cand;
 };
 
 // Element count of one 16-byte weight vector.
@@ -125,8 +130,12 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // NR weight rows per row group (SILU: NR / 2 gate rows j and the matching up
 // rows F + j), R activation rows per launch tile (blockIdx.y), 4 waves per
 // block: 4 row groups (KS = 1) or one row group split over K (KS = 4).
-template <int WT, int XT, int R, int NR, bool SILU, int KS>
+// GATHER (R = 1): the row group's NR outputs are the entries o0 .. o0 + NR of
+// the activation row's candidate list, and their weight rows are the listed
+// ones; everything else, the summation order included, is the dense path's.
+template <int WT, int XT, int R, int NR, bool SILU, int KS, bool GATHER = false>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
+  static_assert(!GATHER || (R == 1 && !SILU), "gathered rows: one activation row, no silu pair");
   constexpr int E = WV<WT>::E;
   constexpr int NP = SILU ? NR / 2 : NR;  // outputs per row group
   const int wib = threadIdx.x >> 6;
@@ -134,15 +143,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
   const int wave = KS == 1 ? blockIdx.x * 4 + wib : blockIdx.x;   // row group
   const int l = lane_id();
   const int o0 = wave * NP;  // first output of this wave
-  if (o0 >= P.n_out) return;
   const int r0 = blockIdx.y * R;
+  int n_out = P.n_out;
+  if constexpr (GATHER) n_out = min(max(P.n_cand[r0], 0), P.max_cand);
+  if (o0 >= n_out) return;  // uniform over the block when KS > 1
   const int F = P.n_out;
   int wrow[NR];
+  bool bad[NR];  // gathered index outside the matrix: row 0 is read, NaN is stored
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    int o = SILU ? (i < NP ? o0 + i : F + o0 + (i - NP)) : o0 + i;
-    const int last = SILU ? (i < NP ? F - 1 : 2 * F - 1) : P.rows - 1;
-    wrow[i] = min(o, last);  // rows past the end repeat the last row; not stored
+    if constexpr (GATHER) {
+      const int j = P.cand[(int64_t)r0 * P.max_cand + min(o0 + i, n_out - 1)];
+      bad[i] = j < 0 || j >= P.rows;
+      wrow[i] = bad[i] ? 0 : j;
+    } else {
+      int o = SILU ? (i < NP ? o0 + i : F + o0 + (i - NP)) : o0 + i;
+      const int last = SILU ? (i < NP ? F - 1 : 2 * F - 1) : P.rows - 1;
+      wrow[i] = min(o, last);  // rows past the end repeat the last row; not stored
+      bad[i] = false;
+    }
   }
   const int64_t row_bytes = (int64_t)P.cols * (WT == 0 ? 4 : WT == 1 ? 2 : 1);
   const int nvec = P.cols / E;
@@ -228,6 +247,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
   }
   const int r = r0 + row;
   if (!writer || r >= P.n_rows) return;
+  if constexpr (GATHER) {
+    float* y = reinterpret_cast<float*>(P.y) + (int64_t)r * P.max_cand;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (o0 + i >= n_out) break;
+      y[o0 + i] = bad[i] ? __builtin_nanf("") : acc[i][0] * P.w_scale;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int o = o0 + i;
@@ -280,6 +308,48 @@ static void launch_w(const GemvParams& P, int xt, bool silu, hipStream_t st) {
   } else {
     if (silu) launch_x<WT, 1, true>(P, st); else launch_x<WT, 1, false>(P, st);
   }
+}
+
+template <int WT, int XT>
+static void launch_gather(const GemvParams& P, hipStream_t st) {
+  constexpr int NR = 4;
+  const int groups = (P.max_cand + NR - 1) / NR;
+  // the dense head's K split for this shape, so each logit has its bits
+  if (gemv_k_split(P.rows, NR) > 1) {
+    hipLaunchKernelGGL((gemv_kernel<WT, XT, 1, NR, false, 4, true>), dim3(groups, P.n_rows), dim3(256), 0, st, P);
+  } else {
+    hipLaunchKernelGGL((gemv_kernel<WT, XT, 1, NR, false, 1, true>), dim3((groups + 3) / 4, P.n_rows), dim3(256), 0,
+                       st, P);
+  }
+}
+
+template <int WT>
+static void launch_gather_w(const GemvParams& P, int xt, hipStream_t st) {
+  if (xt == PKD_F32) launch_gather<WT, 0>(P, st);
+  else launch_gather<WT, 1>(P, st);
+}
+
+pkd_status gemv_gather_launch(const pkd_matrix& W, const void* x, int32_t x_dtype, int32_t n_rows,
+                              const int32_t* cand, const int32_t* n_cand, int32_t max_cand, float* y,
+                              hipStream_t stream, pkd_error* err) {
+  GemvParams P{};
+  P.W = (const uint8_t*)W.data;
+  P.rows = W.rows;
+  P.cols = W.cols;
+  P.w_scale = W.scale;
+  P.x = (const uint8_t*)x;
+  P.x_stride = W.cols;
+  P.n_rows = n_rows;
+  P.y = y;
+  P.n_out = W.rows;
+  P.y_stride = max_cand;
+  P.cand = cand;
+  P.n_cand = n_cand;
+  P.max_cand = max_cand;
+  if (W.dtype == PKD_F32) launch_gather_w<0>(P, x_dtype, stream);
+  else if (W.dtype == PKD_BF16) launch_gather_w<1>(P, x_dtype, stream);
+  else launch_gather_w<2>(P, x_dtype, stream);
+  return check_launch(err, "gemv_gather_rows");
 }
 
 pkd_status gemv_launch(const ProjArgs& a, hipStream_t stream, pkd_error* err) {

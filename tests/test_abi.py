@@ -142,3 +142,29 @@ def test_suggested_k_splits(pkd):
         for m in (1, 64, 768, 4096):
             S = pkd.pkd_suggest_k_splits(rows, cols, 2, m)
             assert S in (1, 2, 3, 4, 6, 8) and (S == 1 or cols // S >= 1536)
+
+
+def test_gather_refusals_are_typed(pkd):
+    """Host-side refusals of the candidate-row head, before any launch."""
+    err = pkd.pkd_error()
+    L = pkd.lib()
+    W = pkd.pkd_matrix(1 << 20, 128, 256, pkd.BF16, 1.0, pkd.FAMILY_MFMA)
+    assert L.gemv_gather_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 2, 1 << 21, 1 << 22, 4, 1 << 23, None,
+                              ctypes.byref(err)) == 2  # matrix-core family
+    W = pkd.pkd_matrix(1 << 20, 1000, 256, pkd.BF16, 1.0, pkd.FAMILY_GEMV)
+    assert L.gemv_gather_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 70000, 1 << 21, 1 << 22, 4, 1 << 23, None,
+                              ctypes.byref(err)) == 2 and err.needed == 70000
+    assert L.gemv_gather_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 2, 1 << 21, 1 << 22, 0, 1 << 23, None,
+                              ctypes.byref(err)) == 1  # max_cand < 1
+    assert L.gemv_gather_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 2, None, 1 << 22, 4, 1 << 23, None,
+                              ctypes.byref(err)) == 1  # no candidate list
+    assert L.gemv_gather_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 2, (1 << 21) + 2, 1 << 22, 4, 1 << 23, None,
+                              ctypes.byref(err)) == 1  # misaligned list
+    assert L.gemv_gather_rows(ctypes.byref(W), (1 << 20) + 4, pkd.BF16, 2, 1 << 21, 1 << 22, 4, 1 << 23, None,
+                              ctypes.byref(err)) == 1  # misaligned activations
+    W = pkd.pkd_matrix(1 << 20, 1000, 100, pkd.BF16, 1.0, pkd.FAMILY_GEMV)
+    assert L.gemv_gather_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 2, 1 << 21, 1 << 22, 4, 1 << 23, None,
+                              ctypes.byref(err)) == 2  # cols not a multiple of 64
+    W = pkd.pkd_matrix(1 << 20, 1000, 256, pkd.BF16, 1.0, pkd.FAMILY_GEMV)
+    assert L.gemv_gather_rows(ctypes.byref(W), None, pkd.BF16, 0, None, None, 0, None, None,
+                              ctypes.byref(err)) == 0  # nothing to do

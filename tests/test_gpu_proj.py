@@ -184,3 +184,118 @@ def test_projection_batch_invariance(H, family, rows):
     perm = torch.randperm(300, generator=torch.Generator().manual_seed(3))
     sh, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, family, x[perm].contiguous(), wl.BF16, 300, wl.F32)
     assert torch.equal(sh.cpu(), full[perm])
+
+
+# ----------------------------------------------------------------------------- gathered rows
+GATHER_CASES = [
+    # (w dtype, x dtype, rows, cols, n rows, max_cand); rows < 32768: K split over
+    # a block's four waves, rows >= 32768: not split (the dense head's choice)
+    (wl.BF16, wl.BF16, 5000, 2048, 1, 28),
+    (wl.BF16, wl.BF16, 5000, 2048, 37, 28),
+    (wl.BF16, wl.F32, 3000, 512, 9, 5),
+    (wl.F32, wl.F32, 1000, 256, 6, 13),
+    (wl.FP8, wl.BF16, 2000, 1024, 20, 28),
+    (wl.FP8, wl.F32, 2000, 1024, 6, 1),
+    (wl.BF16, wl.BF16, 40000, 256, 70, 28),
+    (wl.FP8, wl.BF16, 33000, 512, 16, 33),
+]
+
+
+def gather_lists(n, rows, max_cand, seed):
+    """Trie-shaped candidate lists plus the edge cases: a full list, an empty
+    one, a count above max_cand (clamped), indices outside the matrix (NaN),
+    repeats and the last row."""
+    cand, n_cand = wl.head_candidates(n, rows, max_cand, seed)
+    n_cand[0] = max_cand
+    cand[0] = np.resize(np.array([rows - 1, 0], np.int32), max_cand)  # repeats, both ends
+    if n > 1:
+        n_cand[1] = 0
+    if n > 2:
+        n_cand[2] = max_cand + 5
+        cand[2] = np.arange(max_cand, dtype=np.int32) * 7 % rows
+    if n > 3 and max_cand >= 3:
+        n_cand[3] = 3
+        cand[3, :3] = [-1, rows, rows // 2]
+    return cand, n_cand
+
+
+def run_gather(W, rows, cols, wdt, s, x, xdt, n, cand, n_cand, fill=12345.0):
+    import paged_kv_decode_attn_amd as pkd
+    Wd = W.cuda()  # the matrix descriptor holds a raw pointer: keep the tensor alive
+    M = pkd.make_matrix(Wd, rows, cols, wdt, s, 0)
+    y = torch.full((n, cand.shape[1]), fill, dtype=torch.float32, device="cuda")
+    pkd.gemv_gather_rows(M, x.cuda(), xdt, n, torch.from_numpy(cand).cuda(), torch.from_numpy(n_cand).cuda(),
+                         cand.shape[1], y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def check_gathered(got, want, dense, cand, n_cand, fill):
+    """NaN exactly where the index is bad, the fill where nothing is written,
+    the oracle's value within TOL elsewhere, and the dense head's bits."""
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got == fill, want == fill)
+    ok = np.isfinite(want) & (want != fill)
+    assert ok.any()
+    den = np.abs(want[ok]).max()
+    e = float(np.abs(got[ok] - want[ok]).max() / den)
+    rows = dense.shape[1]
+    for r in range(got.shape[0]):
+        k = int(min(max(n_cand[r], 0), cand.shape[1]))
+        for c in range(k):
+            j = cand[r, c]
+            if 0 <= j < rows:
+                assert got[r, c].tobytes() == np.float64(np.float32(dense[r, j])).tobytes(), (r, c, j)
+    return e
+
+
+@pytest.mark.parametrize("wdt,xdt,rows,cols,n,max_cand", GATHER_CASES)
+def test_gather_parity(H, orc, wdt, xdt, rows, cols, n, max_cand):
+    """Logits of the listed rows: oracle parity, and bit-identical to the same
+    entries of the dense head (gemv_rows over the whole matrix)."""
+    seed = rows + cols + n
+    W, s = make_w(rows, cols, wdt, seed)
+    x = make_x(n, cols, xdt, seed)
+    cand, n_cand = gather_lists(n, rows, max_cand, seed)
+    fill = 12345.0
+    got = run_gather(W, rows, cols, wdt, s, x, xdt, n, cand, n_cand, fill)
+    xv = (orc.bf16_value(wl.to_numpy_codes(x, wl.BF16)) if xdt == wl.BF16 else x.numpy().astype(np.float64))
+    want = orc.matvec_gathered(wdt, wl.to_numpy_codes(W, wdt), s, xv, cand, n_cand, fill)
+    dense, _ = run_proj(H, W, rows, cols, wdt, s, 0, x, xdt, n, wl.F32)
+    e = check_gathered(got, want, dense.cpu().numpy(), cand, n_cand, fill)
+    print(f"gather w{wdt} x{xdt} {rows}x{cols} n={n} max_cand={max_cand}: {e:.2e}")
+    assert e <= TOL
+
+
+def test_gather_full_vocabulary_head(H, orc):
+    """The tied-embedding head at its full size (151,936 x 2,048 bf16), 64
+    rows of up to 28 candidates: every entry bit-identical to the dense head,
+    and the oracle on a sample of rows."""
+    import paged_kv_decode_attn_amd as pkd
+    V, D, C = wl.HEAD_VOCAB, wl.HEAD_HIDDEN, wl.HEAD_MAX_CAND
+    n = 64
+    g = torch.Generator(device="cuda").manual_seed(77)
+    Wd = (torch.randn((V, D), generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
+    x = (torch.randn((n, D), generator=g, device="cuda")).to(torch.bfloat16).view(torch.int16)
+    cand, n_cand = wl.head_candidates(n, V, C, 78)
+    M = pkd.make_matrix(Wd, V, D, wl.BF16, 1.0, 0)
+    y = torch.full((n, C), -5.0, device="cuda")
+    pkd.gemv_gather_rows(M, x, wl.BF16, n, torch.from_numpy(cand).cuda(), torch.from_numpy(n_cand).cuda(), C, y)
+    dense = torch.empty((n, V), device="cuda")
+    pkd.gemv_rows(M, x, wl.BF16, n, dense, wl.F32)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    dn = dense.cpu().numpy()
+    for r in range(n):
+        k = n_cand[r]
+        assert np.array_equal(got[r, :k].view(np.uint32), dn[r, cand[r, :k]].view(np.uint32)), r
+        assert (got[r, k:] == -5.0).all()
+    rs = [0, 1, 31, n - 1]
+    sub = np.unique(cand[rs][cand[rs] >= 0])
+    Wsub = Wd[torch.from_numpy(sub).long().cuda()].cpu().numpy().view(np.uint16)
+    remap = np.searchsorted(sub, np.where(cand[rs] >= 0, cand[rs], sub[0])).astype(np.int32)
+    xv = orc.bf16_value(x[rs].cpu().numpy().view(np.uint16))
+    want = orc.matvec_gathered(wl.BF16, Wsub, 1.0, xv, remap, n_cand[rs], -5.0)
+    e = H.rel_err(got[rs], want)
+    print(f"full head n={n}: {e:.2e}")
+    assert e <= TOL

@@ -428,3 +428,24 @@ def history_lists(w: Workload, seqs=None):
         hk.append(to_numpy_codes(w.hist_k[o:o + L], w.kv_dtype))
         hv.append(to_numpy_codes(w.hist_v[o:o + L], w.kv_dtype))
     return hk, hv
+
+
+# ----------------------------------------------------------------------------- output head
+# A tied embedding of 151,936 rows by 2,048 bf16 columns is 593.5 MiB and 28
+# of its rows are 112 KiB: the full-head and candidate-head read sizes of the
+# grammar-bounded output layer ("GPU inference engine engineering", headline
+# figure "Grammar-bounded output", at most 28 edges per trie node).
+HEAD_VOCAB, HEAD_HIDDEN, HEAD_MAX_CAND = 151936, 2048, 28
+
+
+def head_candidates(n: int, vocab: int, max_cand: int = HEAD_MAX_CAND, seed: int = 0):
+    """Per-row candidate lists shaped like a trie node's outgoing edges:
+    1 .. max_cand distinct rows of the vocabulary (count uniform), in random
+    order; unused slots hold -1.  Returns (cand int32 [n][max_cand],
+    n_cand int32 [n]) as numpy arrays."""
+    rng = np.random.default_rng(seed)
+    cand = np.full((n, max_cand), -1, np.int32)
+    n_cand = rng.integers(1, max_cand + 1, size=n).astype(np.int32)
+    for r in range(n):
+        cand[r, :n_cand[r]] = rng.choice(vocab, size=n_cand[r], replace=False)
+    return cand, n_cand
