@@ -26,6 +26,9 @@
  *     rounding, so the oracle is the plain definition.
  *   - FFN: silu(W_gate h) * (W_up h), gate/up fused as in "llm-rs" section 3;
  *     residuals h = x + W_o attn and y = h + W_down a.
+ *   - optional RMSNorm before attention and before the FFN, gains folded into
+ *     W_qkv and W_gate_up ("llm-rs", section 4, third lesson), and optional
+ *     rotary positions on q and k (a reading: the pages never describe them).
  * Readings where the pages are silent (softmax scale, GQA mapping, rounding
  * points, residual form, fp8 activation scaling) are listed with the build's
  * design notes; each is marked where it is used below.
@@ -433,6 +436,45 @@ int orc_attention(const orc_attn_geom* G, const orc_history* H, int n_rows, cons
 }
 
 /* ------------------------------------------------------------------------ */
+/* Norm factor and rotary positions (the steps on either side of the path)   */
+/* ------------------------------------------------------------------------ */
+
+/* RMSNorm's per-row factor 1 / sqrt(mean_k z[k]^2 + eps).  The norm's gain is
+ * folded into the following projection's weights, so at step time only this
+ * scalar remains, applied to the projection's outputs ("llm-rs", section 4,
+ * third lesson: norms folded into the projections). */
+double orc_inv_rms(const double* z, int cols, double eps) {
+  double ss = 0.0;
+  for (int k = 0; k < cols; ++k) ss += z[k] * z[k];
+  return 1.0 / sqrt(ss / cols + eps);
+}
+
+void orc_inv_rms_rows(const double* Z, int n, int cols, double eps, double* out) {
+  for (int r = 0; r < n; ++r) out[r] = orc_inv_rms(Z + (int64_t)r * cols, cols, eps);
+}
+
+/* Rotary position embedding (reading; the pages are silent): within each head
+ * of width hd, the consecutive pair (v[2i], v[2i+1]) is rotated by the angle
+ * pos * base^(-2i / hd):
+ *   v[2i]   <- v[2i] cos - v[2i+1] sin,   v[2i+1] <- v[2i] sin + v[2i+1] cos. */
+void orc_rope(double* v, int n_heads, int hd, int pos, double base) {
+  for (int i = 0; i < hd / 2; ++i) {
+    double theta = (double)pos * pow(base, -2.0 * i / hd);
+    double c = cos(theta), sn = sin(theta);
+    for (int h = 0; h < n_heads; ++h) {
+      double* e = v + (int64_t)h * hd + 2 * i;
+      double a = e[0], b = e[1];
+      e[0] = a * c - b * sn;
+      e[1] = a * sn + b * c;
+    }
+  }
+}
+
+void orc_rope_rows(double* V, int n, int n_heads, int hd, const int32_t* pos, double base) {
+  for (int r = 0; r < n; ++r) orc_rope(V + (int64_t)r * n_heads * hd, n_heads, hd, pos[r], base);
+}
+
+/* ------------------------------------------------------------------------ */
 /* One decode step of one layer                                              */
 /* ------------------------------------------------------------------------ */
 
@@ -445,7 +487,12 @@ typedef struct {
   int32_t act_fp8;                      /* 1: projection inputs quantised per row to fp8 */
   int32_t kv_dtype;
   float k_scale, v_scale;
+  int32_t flags;      /* ORC_NORM: RMSNorm before attention and FFN; ORC_ROPE: rotate q, k */
+  double norm_eps;    /* RMSNorm epsilon */
+  double rope_base;   /* RoPE base */
 } orc_layer;
+
+enum { ORC_NORM = 1, ORC_ROPE = 2 };
 
 typedef struct {
   double *qkv, *attn, *h, *a, *y; /* [n][...] outputs, any may be NULL */
@@ -499,8 +546,19 @@ int orc_decode_step(const orc_layer* L, const orc_history* H, int n, const int32
   if (!xd || !qkv || !qv || !kv || !vv || !att || !ao || !h) goto done;
   for (int64_t i = 0; i < (int64_t)n * D; ++i) xd[i] = (double)x[i];
 
-  /* qkv = W_qkv x, stored in the activation dtype */
+  /* qkv = W_qkv x, stored in the activation dtype.  With the norm, W_qkv
+   * carries the pre-attention gain and the outputs are scaled by the row's
+   * 1/rms(x); with RoPE, the q and k heads are rotated by the row's position
+   * before the rounding. */
   if (project(L, L->w_qkv, L->s_qkv, nqkv, D, xd, n, qkv)) goto done;
+  for (int r = 0; r < n; ++r) {
+    double* row = qkv + (int64_t)r * nqkv;
+    if (L->flags & ORC_NORM) {
+      double f = orc_inv_rms(xd + (int64_t)r * D, D, L->norm_eps);
+      for (int j = 0; j < nqkv; ++j) row[j] *= f;
+    }
+    if (L->flags & ORC_ROPE) orc_rope(row, nq + nkv, d, pos[r], L->rope_base);
+  }
   for (int64_t i = 0; i < (int64_t)n * nqkv; ++i) qkv[i] = round_act(qkv[i], L->act_dtype);
   for (int r = 0; r < n; ++r) {
     const double* row = qkv + (int64_t)r * nqkv;
@@ -527,11 +585,14 @@ int orc_decode_step(const orc_layer* L, const orc_history* H, int n, const int32
     dn = (double*)malloc(sizeof(double) * nn * D);
     if (!gu || !a || !dn) goto done;
     if (project(L, L->w_gu, L->s_gu, 2 * F, D, h, n, gu)) goto done;
-    for (int r = 0; r < n; ++r)
+    for (int r = 0; r < n; ++r) {
+      /* pre-FFN norm: gain in W_gate_up, 1/rms(h) on both halves before silu */
+      double f = (L->flags & ORC_NORM) ? orc_inv_rms(h + (int64_t)r * D, D, L->norm_eps) : 1.0;
       for (int j = 0; j < F; ++j) {
-        double g = gu[(int64_t)r * 2 * F + j], u = gu[(int64_t)r * 2 * F + F + j];
+        double g = gu[(int64_t)r * 2 * F + j] * f, u = gu[(int64_t)r * 2 * F + F + j] * f;
         a[(int64_t)r * F + j] = round_act(g / (1.0 + exp(-g)) * u, L->act_dtype);
       }
+    }
     if (out && out->a) memcpy(out->a, a, sizeof(double) * n * F);
     if (project(L, L->w_d, L->s_d, D, F, a, n, dn)) goto done;
     if (out && out->y)

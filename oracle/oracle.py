@@ -18,6 +18,7 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 F32, BF16, FP8 = 0, 1, 2
+NORM, ROPE = 1, 2
 _NP = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
 
 
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.orc_matvec_gathered.argtypes = [ctypes.c_int, P, ctypes.c_double, ctypes.c_int, ctypes.c_int, P,
                                           ctypes.c_int, P, ctypes.c_int, P, P]
         L.orc_matvec_gathered.restype = None
+        L.orc_inv_rms_rows.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_double, P]
+        L.orc_inv_rms_rows.restype = None
+        L.orc_rope_rows.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_double]
+        L.orc_rope_rows.restype = None
         L.orc_gather_history.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P,
                                          ctypes.c_int, ctypes.c_int, P, P]
         L.orc_gather_history.restype = ctypes.c_int
@@ -161,6 +166,23 @@ def matvec_gathered(dtype: int, W: np.ndarray, scale: float, X: np.ndarray, cand
     return Y
 
 
+def inv_rms_rows(Z: np.ndarray, eps: float) -> np.ndarray:
+    """1 / sqrt(mean(z^2) + eps) per row of Z, in fp64."""
+    Z = _c(Z, np.float64)
+    Z2 = Z.reshape(Z.shape[0], -1)
+    out = np.empty(Z2.shape[0], np.float64)
+    lib().orc_inv_rms_rows(_ptr(Z2), Z2.shape[0], Z2.shape[1], float(eps), _ptr(out))
+    return out
+
+
+def rope_rows(V: np.ndarray, n_heads: int, hd: int, pos, base: float) -> np.ndarray:
+    """Rotary positions on rows of V [n][n_heads * hd] (consecutive pairs), fp64."""
+    V = np.array(V, dtype=np.float64, order="C", copy=True).reshape(-1, n_heads * hd)
+    pos = _c(pos, np.int32)
+    lib().orc_rope_rows(_ptr(V), V.shape[0], n_heads, hd, _ptr(pos), float(base))
+    return V
+
+
 # ---------------------------------------------------------------- structs
 class _Geom(ctypes.Structure):
     _fields_ = [("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -181,7 +203,8 @@ class _Layer(ctypes.Structure):
                 ("s_qkv", ctypes.c_double), ("s_o", ctypes.c_double), ("s_gu", ctypes.c_double),
                 ("s_d", ctypes.c_double), ("act_dtype", ctypes.c_int32),
                 ("act_fp8", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("flags", ctypes.c_int32), ("norm_eps", ctypes.c_double), ("rope_base", ctypes.c_double)]
 
 
 class _Out(ctypes.Structure):
@@ -248,7 +271,9 @@ def gather_history(pages: np.ndarray, n_kv: int, d: int, kv_dtype: int, table_ro
 
 def decode_step(layer: dict, hist: History, seq, pos, x) -> dict:
     """layer: hidden, n_q, n_kv, head_dim, ffn, w_dtype, w_qkv, w_o, w_gu, w_d (code
-    arrays), s_qkv, s_o, s_gu, s_d, act_dtype, act_fp8, kv_dtype, k_scale, v_scale."""
+    arrays), s_qkv, s_o, s_gu, s_d, act_dtype, act_fp8, kv_dtype, k_scale, v_scale;
+    optional norm (bool, gains already folded into w_qkv / w_gu), norm_eps,
+    rope (bool), rope_base."""
     seq = _c(seq, np.int32)
     pos = _c(pos, np.int32)
     x = _c(x, np.float32)
@@ -261,7 +286,9 @@ def decode_step(layer: dict, hist: History, seq, pos, x) -> dict:
                float(layer.get("s_qkv", 1.0)), float(layer.get("s_o", 1.0)),
                float(layer.get("s_gu", 1.0)), float(layer.get("s_d", 1.0)),
                layer["act_dtype"], int(layer.get("act_fp8", 0)), layer["kv_dtype"],
-               float(layer.get("k_scale", 1.0)), float(layer.get("v_scale", 1.0)))
+               float(layer.get("k_scale", 1.0)), float(layer.get("v_scale", 1.0)),
+               (NORM if layer.get("norm") else 0) | (ROPE if layer.get("rope") else 0),
+               float(layer.get("norm_eps", 1e-6)), float(layer.get("rope_base", 10000.0)))
     outs = {"qkv": np.empty((n, (nq + 2 * nkv) * d)), "attn": np.empty((n, nq * d)),
             "h": np.empty((n, D)), "y": np.empty((n, D))}
     if F > 0:

@@ -401,6 +401,48 @@ def test_fp8_append_rounding_is_fp32_division(orc):
     assert np.all(out == 1.25 * ks)
 
 
+# ----------------------------------------------------------------------------- norm and rotary positions
+def test_inv_rms_definition(orc):
+    """The norm factor against torch's RMSNorm (no gain) in fp64, closed forms
+    for constant and zero rows, and exact homogeneity at eps = 0."""
+    rng = np.random.default_rng(30)
+    Z = rng.standard_normal((5, 96))
+    eps = 1e-6
+    f = orc.inv_rms_rows(Z, eps)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(Z), (96,), eps=eps).numpy()
+    assert np.allclose(Z * f[:, None], want, rtol=1e-14, atol=1e-15)
+    assert math.isclose(orc.inv_rms_rows(np.full((1, 64), 3.0), 0.5)[0], 1 / math.sqrt(9.5), rel_tol=1e-15)
+    assert np.allclose(orc.inv_rms_rows(4.0 * Z, 0.0), orc.inv_rms_rows(Z, 0.0) / 4.0, rtol=1e-15, atol=0)
+    assert orc.inv_rms_rows(np.zeros((1, 64)), 1e-6)[0] == 1 / math.sqrt(1e-6)
+
+
+def test_rope_definition(orc):
+    """Rotary positions: identity at position 0; pair i of each head equals the
+    complex product (v[2i] + i v[2i+1]) e^(i theta); closed-form angles
+    (pair 0 turns by pos radians; hd = 4, base 100: pair 1 by pos / 10);
+    q . k depends on the two positions only through their difference."""
+    rng = np.random.default_rng(31)
+    nh, hd = 3, 16
+    V = rng.standard_normal((4, nh * hd))
+    pos = np.array([0, 1, 37, 2661], np.int32)
+    R = orc.rope_rows(V, nh, hd, pos, 10000.0)
+    assert np.array_equal(R[0], V[0])
+    for r in range(4):
+        z = V[r].reshape(nh, hd // 2, 2) @ np.array([1, 1j])
+        w = z * np.exp(1j * pos[r] * 10000.0 ** (-np.arange(hd // 2) * 2.0 / hd))
+        got = R[r].reshape(nh, hd // 2, 2)
+        assert np.allclose(got[..., 0], w.real, rtol=0, atol=1e-12)
+        assert np.allclose(got[..., 1], w.imag, rtol=0, atol=1e-12)
+    e = orc.rope_rows(np.array([[1.0, 0.0, 1.0, 0.0]]), 1, 4, [10], 100.0)[0]
+    assert np.allclose(e, [math.cos(10), math.sin(10), math.cos(1), math.sin(1)], rtol=0, atol=1e-15)
+    q, k = rng.standard_normal((2, hd))
+
+    def dot(pq, pk):
+        return orc.rope_rows(q[None], 1, hd, [pq], 500.0)[0] @ orc.rope_rows(k[None], 1, hd, [pk], 500.0)[0]
+    for pq, pk, t in [(5, 2, 11), (100, 0, 900), (7, 7, 3)]:
+        assert math.isclose(dot(pq, pk), dot(pq + t, pk + t), rel_tol=1e-10, abs_tol=1e-12)
+
+
 # ----------------------------------------------------------------------------- decode step
 def _small_layer(orc, rng, w_dtype=1, kv_dtype=1, act_fp8=0, D=128, nq=4, nkv=2, d=64, F=256,
                  lens=(1, 5, 33, 64, 70)):
@@ -505,6 +547,62 @@ def test_step_vs_torch_composition(orc):
     assert np.allclose(out["y"], y.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def _fold_gains(layer, rng):
+    """Turns on the norm and rotary positions and folds random norm gains into
+    the f32 W_qkv and W_gate_up columns; returns the two gain vectors."""
+    D = layer["hidden"]
+    g1 = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    g2 = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    layer["w_qkv"] = (layer["w_qkv"].astype(np.float32) * g1[None, :]).astype(np.float32)
+    layer["w_gu"] = (layer["w_gu"].astype(np.float32) * g2[None, :]).astype(np.float32)
+    layer.update(norm=True, rope=True, norm_eps=1e-6, rope_base=10000.0)
+    return g1, g2
+
+
+def test_step_norm_rope_vs_torch_composition(orc):
+    """f32 tier with RMSNorm and rotary positions, against torch fp64: rms_norm
+    with the gain and the unfolded weights, the rotation as a complex product,
+    scaled_dot_product_attention, silu; f32 rounding at the same points."""
+    rng = np.random.default_rng(26)
+    layer, hist, seq, pos, x = _small_layer(orc, rng, w_dtype=0, kv_dtype=0)
+    W0 = {k: layer[k].astype(np.float64) for k in ("w_qkv", "w_o", "w_gu", "w_d")}
+    g1, g2 = _fold_gains(layer, rng)
+    D, nq, nkv, d, F = (layer[k] for k in ("hidden", "n_q", "n_kv", "head_dim", "ffn"))
+    out = orc.decode_step(layer, hist, seq, pos, x)
+
+    def f32(t):
+        return t.float().double()
+    X = torch.from_numpy(x).double()
+    xn = torch.nn.functional.rms_norm(X, (D,), weight=torch.from_numpy(g1).double(), eps=1e-6)
+    qkv = (xn @ torch.from_numpy(W0["w_qkv"]).T).numpy()
+    for r in range(len(seq)):
+        z = qkv[r, :(nq + nkv) * d].reshape(nq + nkv, d // 2, 2) @ np.array([1, 1j])
+        z = z * np.exp(1j * pos[r] * 10000.0 ** (-np.arange(d // 2) * 2.0 / d))
+        qkv[r, :(nq + nkv) * d] = np.stack([z.real, z.imag], -1).reshape(-1)
+    qkv = f32(torch.from_numpy(qkv))
+    assert np.allclose(out["qkv"], qkv.numpy(), rtol=1e-6, atol=1e-7)
+    qkv = torch.from_numpy(out["qkv"])
+    att = []
+    for r in range(len(seq)):
+        o, L = hist.hist_off[r], hist.hist_len[r]
+        Kh = torch.from_numpy(hist.k[o:o + L].astype(np.float64))
+        Vh = torch.from_numpy(hist.v[o:o + L].astype(np.float64))
+        kn = qkv[r, nq * d:(nq + nkv) * d].reshape(1, nkv, d)
+        vn = qkv[r, (nq + nkv) * d:].reshape(1, nkv, d)
+        K = torch.cat([Kh, kn]).permute(1, 0, 2).repeat_interleave(nq // nkv, 0)
+        V = torch.cat([Vh, vn]).permute(1, 0, 2).repeat_interleave(nq // nkv, 0)
+        qh = qkv[r, :nq * d].reshape(nq, 1, d)
+        att.append(torch.nn.functional.scaled_dot_product_attention(qh, K, V)[:, 0].reshape(-1))
+    att = f32(torch.stack(att))
+    assert np.allclose(out["attn"], att.numpy(), rtol=1e-6, atol=1e-7)
+    h = X + torch.from_numpy(out["attn"]) @ torch.from_numpy(W0["w_o"]).T
+    assert np.allclose(out["h"], h.numpy(), rtol=1e-10, atol=1e-12)
+    hn = torch.nn.functional.rms_norm(f32(h), (D,), weight=torch.from_numpy(g2).double(), eps=1e-6)
+    gu = hn @ torch.from_numpy(W0["w_gu"]).T
+    a = f32(torch.nn.functional.silu(gu[:, :F]) * gu[:, F:])
+    assert np.allclose(out["a"], a.numpy(), rtol=1e-6, atol=1e-7)
+
+
 def test_step_fp8_tier_projection(orc):
     """fp8 matrix-core tier: a projection is s_z * s_W * sum(z8 * W8) with the
     input quantised per row; checked on W_qkv against numpy on decoded codes."""
@@ -519,11 +617,15 @@ def test_step_fp8_tier_projection(orc):
         assert np.allclose(got, want, rtol=2 ** -7, atol=1e-6)
 
 
-def test_step_rows_independent_and_sequential(orc):
+@pytest.mark.parametrize("norm_rope", [False, True])
+def test_step_rows_independent_and_sequential(orc, norm_rope):
     """Rows are independent (any order, alone) and several rows of one sequence
-    in one step equal the same rows run one step at a time."""
+    in one step equal the same rows run one step at a time (with rotary
+    positions too: the stored keys are the rotated ones)."""
     rng = np.random.default_rng(25)
     layer, hist, seq, pos, x = _small_layer(orc, rng)
+    if norm_rope:
+        layer.update(norm=True, rope=True, norm_eps=1e-6, rope_base=10000.0)
     full = orc.decode_step(layer, hist, seq, pos, x)
     perm = np.asarray([4, 2, 0, 3, 1])
     sh = orc.decode_step(layer, hist, seq[perm], pos[perm], x[perm])
