@@ -292,6 +292,17 @@ typedef struct {
  *                   y[r][j] = silu(acc[r][j]) * acc[r][F + j], j < F
  *                   ([LRS] section 3: gate and up projections fused with
  *                   their activation); residual must be NULL.
+ * Before the silu / residual step, acc (already times the weight scale) is
+ *   multiplied by row_scale[r] when row_scale is not NULL (device f32 [n]:
+ *   the 1/rms factor of a norm whose gain is folded into W, "llm-rs"
+ *   section 4, third lesson: norms folded into the projections), and
+ *   rotated in consecutive pairs when rope_cs is not NULL: for columns
+ *   j < rope_cols, pair (2i, 2i+1) of each head of rope_head_dim columns
+ *   (i = (j mod rope_head_dim) / 2) becomes
+ *     (a c - b s, a s + b c),  (c, s) = rope_cs[r][i]  (device f32
+ *   [n][rope_head_dim / 2][2], e.g. from rope_table).  rope_head_dim must be
+ *   a positive multiple of 4, rope_cols a multiple of it and at most the
+ *   output count; rotation and silu_pair exclude each other.
  * out_dtype f32 or bf16.  residual: NULL or device f32 [n][rows].
  * y_bf16: NULL, or a second output that receives y rounded to bf16 (the
  * input of a following bf16 projection).
@@ -301,6 +312,10 @@ typedef struct {
   const float* residual;
   int32_t silu_pair;
   void* y_bf16;
+  const float* row_scale;
+  const float* rope_cs;
+  int32_t rope_cols;
+  int32_t rope_head_dim;
 } pkd_epilogue;
 
 size_t pkd_gemv_workspace_bytes(const pkd_matrix* W, int32_t max_rows);
@@ -363,6 +378,35 @@ pkd_status gemv_gather_rows(const pkd_matrix* W, const void* x, int32_t x_dtype,
                             const int32_t* cand, const int32_t* n_cand, int32_t max_cand, float* y,
                             pkd_stream stream, pkd_error* err);
 
+/*
+ * RMSNorm factor of each row, the part of a norm that remains at step time
+ * once its gain is folded into the next projection's weight columns ("llm-rs",
+ * section 4, third lesson: norms folded into the projections):
+ *   inv_rms[r] = 1 / sqrt(sum_k x[r][k]^2 / cols + eps)
+ * computed in fp32 in a fixed order (a row's value never depends on n_rows).
+ * x: device f32 [n_rows][cols], cols a positive multiple of 4, 16-byte
+ * aligned.  x_bf16: NULL, or device [n_rows][cols] bf16 that receives x
+ * rounded to nearest even (16-byte aligned).  inv_rms: device f32 [n_rows].
+ * Errors: bad sizes, eps < 0 or not finite, NULL or misaligned pointers ->
+ * PKD_ERR_INVALID_ARG / PKD_ERR_UNSUPPORTED, before any launch.
+ */
+pkd_status rms_norm_factor(const float* x, int32_t n_rows, int32_t cols, float eps, float* inv_rms,
+                           void* x_bf16, pkd_stream stream, pkd_error* err);
+
+/*
+ * Rotary-position table for the epilogue's rotation (the pages do not
+ * describe positional encoding; this is the consecutive-pair form):
+ *   cs[r][i] = (cos t, sin t),  t = pos[r] * base^(-2 i / head_dim),
+ * for i < head_dim / 2, evaluated in fp64 and stored as f32.
+ * pos: device int32 [n_rows]; cs: device f32 [n_rows][head_dim / 2][2].
+ * head_dim even and >= 2, base finite and > 0, else PKD_ERR_INVALID_ARG.
+ * Checkpoints that rotate the halves (i, i + head_dim / 2) instead can be used
+ * by permuting the q and k rows of W_qkv within each head to pair order, which
+ * leaves every q . k unchanged.
+ */
+pkd_status rope_table(const int32_t* pos, int32_t n_rows, int32_t head_dim, float base, float* cs,
+                      pkd_stream stream, pkd_error* err);
+
 /* ------------------------------------------------------------------------ */
 /* One decode step of one transformer layer                                  */
 /* ------------------------------------------------------------------------ */
@@ -383,7 +427,17 @@ typedef struct {
   pkd_matrix w_gate_up; /* [2F][D] = [W_gate; W_up] */
   pkd_matrix w_down;  /* [D][F] */
   int32_t act_dtype;
+  int32_t flags;      /* PKD_LAYER_NORM | PKD_LAYER_ROPE, or 0 */
+  float norm_eps;     /* PKD_LAYER_NORM: the norms' epsilon (>= 0) */
+  float rope_base;    /* PKD_LAYER_ROPE: the rotary base (> 0) */
 } pkd_layer;
+
+/* PKD_LAYER_NORM: RMSNorm before attention and before the FFN, with their
+ * gains already folded into the columns of w_qkv and w_gate_up; the step
+ * applies 1/rms(x) to the qkv outputs and 1/rms(h) to both gate/up halves
+ * before the silu.  PKD_LAYER_ROPE: q and k heads rotated by the row's
+ * position (rope_table's angles) before they are stored or attended. */
+enum { PKD_LAYER_NORM = 1, PKD_LAYER_ROPE = 2 };
 
 size_t pkd_step_workspace_bytes(const pkd_layer* layer, const pkd_pool* pool, int32_t max_rows);
 
@@ -394,8 +448,10 @@ size_t pkd_step_workspace_bytes(const pkd_layer* layer, const pkd_pool* pool, in
  *   a   = silu(W_gate h) * (W_up h)          (when ffn > 0)
  *   y   = h + W_down a                       (y = h when ffn = 0)
  * x and y are device f32 [n][hidden].  Every projection input is taken in
- * act_dtype.  Token embedding, normalisation and positional encoding are not
- * part of this step.
+ * act_dtype.  With PKD_LAYER_NORM / PKD_LAYER_ROPE (layer->flags):
+ *   qkv = (W_qkv x) / rms(x), then q and k rotated by pos ; a = silu(W_gate h
+ *   / rms(h)) * (W_up h / rms(h)), with the norm gains folded into W_qkv and
+ *   W_gate_up by the caller.  Token embedding is not part of this step.
  */
 pkd_status decode_step(const pkd_layer* layer, pkd_pool* pool, const pkd_rows* rows,
                        const float* x, float* y, void* ws, size_t ws_bytes,

@@ -67,19 +67,26 @@ class pkd_matrix(ctypes.Structure):
 
 class pkd_epilogue(ctypes.Structure):
     _fields_ = [("out_dtype", ctypes.c_int32), ("residual", ctypes.c_void_p),
-                ("silu_pair", ctypes.c_int32), ("y_bf16", ctypes.c_void_p)]
+                ("silu_pair", ctypes.c_int32), ("y_bf16", ctypes.c_void_p),
+                ("row_scale", ctypes.c_void_p), ("rope_cs", ctypes.c_void_p),
+                ("rope_cols", ctypes.c_int32), ("rope_head_dim", ctypes.c_int32)]
 
 
 class pkd_layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("w_qkv", pkd_matrix), ("w_o", pkd_matrix), ("w_gate_up", pkd_matrix),
-                ("w_down", pkd_matrix), ("act_dtype", ctypes.c_int32)]
+                ("w_down", pkd_matrix), ("act_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+LAYER_NORM, LAYER_ROPE = 1, 2
 
 
 EXPORTS = ["pkd_pool_bytes", "kv_pool_create", "kv_pool_destroy", "pkd_pool_info_get", "block_table_set",
            "pkd_pool_check", "pkd_attn_workspace_bytes", "paged_attn_decode", "pkd_gemv_workspace_bytes",
-           "pkd_suggest_k_splits", "gemv_rows", "gemv_gather_rows", "pkd_step_workspace_bytes", "decode_step", "pkd_status_string", "pkd_version"]
+           "pkd_suggest_k_splits", "gemv_rows", "gemv_gather_rows", "rms_norm_factor", "rope_table",
+           "pkd_step_workspace_bytes", "decode_step", "pkd_status_string", "pkd_version"]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -103,6 +110,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gemv_rows": (I32, [ctypes.POINTER(pkd_matrix), P, I32, I32, P, ctypes.POINTER(pkd_epilogue), P, SZ,
                             P, E]),
         "gemv_gather_rows": (I32, [ctypes.POINTER(pkd_matrix), P, I32, I32, P, P, I32, P, P, E]),
+        "rms_norm_factor": (I32, [P, I32, I32, ctypes.c_float, P, P, P, E]),
+        "rope_table": (I32, [P, I32, I32, ctypes.c_float, P, P, E]),
         "pkd_step_workspace_bytes": (SZ, [ctypes.POINTER(pkd_layer), P, I32]),
         "decode_step": (I32, [ctypes.POINTER(pkd_layer), P, ctypes.POINTER(pkd_rows), P, P, P, SZ, P, E]),
         "pkd_status_string": (ctypes.c_char_p, [I32]),
@@ -220,8 +229,10 @@ def pkd_suggest_k_splits(rows: int, cols: int, family: int, typical_rows: int) -
 
 
 def gemv_rows(W: pkd_matrix, x, x_dtype: int, n_rows: int, y, out_dtype: int = F32, residual=None,
-              silu_pair: bool = False, y_bf16=None, ws=None, stream=None) -> None:
-    ep = pkd_epilogue(out_dtype, _ptr(residual), 1 if silu_pair else 0, _ptr(y_bf16))
+              silu_pair: bool = False, y_bf16=None, ws=None, stream=None, row_scale=None, rope_cs=None,
+              rope_cols: int = 0, rope_head_dim: int = 0) -> None:
+    ep = pkd_epilogue(out_dtype, _ptr(residual), 1 if silu_pair else 0, _ptr(y_bf16), _ptr(row_scale),
+                      _ptr(rope_cs), rope_cols, rope_head_dim)
     err = pkd_error()
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gemv_rows(ctypes.byref(W), _ptr(x), x_dtype, n_rows, _ptr(y), ctypes.byref(ep), _ptr(ws),
@@ -234,6 +245,19 @@ def gemv_gather_rows(W: pkd_matrix, x, x_dtype: int, n_rows: int, cand, n_cand, 
     err = pkd_error()
     _check(lib().gemv_gather_rows(ctypes.byref(W), _ptr(x), x_dtype, n_rows, _ptr(cand), _ptr(n_cand), max_cand,
                                   _ptr(y), _stream(stream), ctypes.byref(err)), err)
+
+
+def rms_norm_factor(x, n_rows: int, cols: int, eps: float, inv_rms, x_bf16=None, stream=None) -> None:
+    """inv_rms[r] = 1 / sqrt(mean(x[r]^2) + eps); optionally x rounded to bf16."""
+    err = pkd_error()
+    _check(lib().rms_norm_factor(_ptr(x), n_rows, cols, eps, _ptr(inv_rms), _ptr(x_bf16), _stream(stream),
+                                 ctypes.byref(err)), err)
+
+
+def rope_table(pos, n_rows: int, head_dim: int, base: float, cs, stream=None) -> None:
+    """cs[r][i] = (cos, sin) of pos[r] * base^(-2i / head_dim)."""
+    err = pkd_error()
+    _check(lib().rope_table(_ptr(pos), n_rows, head_dim, base, _ptr(cs), _stream(stream), ctypes.byref(err)), err)
 
 
 # ------------------------------------------------------------------ decode step

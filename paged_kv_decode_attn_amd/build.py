@@ -8,7 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkd.so")
-SOURCES = ["api.hip", "attention.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "attention.hip", "gemv.hip", "gemm.hip", "rowprep.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

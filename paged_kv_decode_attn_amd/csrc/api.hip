@@ -133,6 +133,16 @@ pkd_status proj_validate(const ProjArgs& a, pkd_error* err) {
   if (a.silu_pair && (W->rows % 2 || a.residual))
     return fail(err, PKD_ERR_INVALID_ARG, W->rows, 0, "silu_pair needs an even row count and no residual");
   if (a.n_rows > 0 && (!a.x || !a.y)) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "x or y is NULL");
+  if (a.rope_cs) {
+    const int n_out = a.silu_pair ? W->rows / 2 : W->rows;
+    if (a.silu_pair) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "rotary pairs and silu_pair exclude each other");
+    if (a.rope_hd < 4 || a.rope_hd % 4 || a.rope_cols < 0 || a.rope_cols % a.rope_hd || a.rope_cols > n_out)
+      return fail(err, PKD_ERR_INVALID_ARG, a.rope_cols, n_out,
+                  "rope_head_dim %d must be a positive multiple of 4 and rope_cols %d a multiple of it, at most %d",
+                  a.rope_hd, a.rope_cols, n_out);
+  }
+  if (((uintptr_t)a.row_scale & 3) || ((uintptr_t)a.rope_cs & 7))
+    return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "row_scale must be 4-byte and rope_cs 8-byte aligned");
   if (!aligned16(a.x) || !aligned16(a.y) || !aligned16(a.residual) || !aligned16(a.y_bf16))
     return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "device pointers must be 16-byte aligned");
   if (W->family != PKD_FAMILY_GEMV) {
@@ -355,6 +365,10 @@ pkd_status gemv_rows(const pkd_matrix* W, const void* x, int32_t x_dtype, int32_
   a.residual = ep->residual;
   a.silu_pair = ep->silu_pair;
   a.y_bf16 = ep->y_bf16;
+  a.row_scale = ep->row_scale;
+  a.rope_cs = ep->rope_cs;
+  a.rope_cols = ep->rope_cols;
+  a.rope_hd = ep->rope_head_dim;
   pkd_status s = proj_validate(a, err);
   if (s != PKD_OK) return s;
   return proj_launch(a, ws, ws_bytes, (hipStream_t)stream, err);
@@ -384,6 +398,30 @@ pkd_status gemv_gather_rows(const pkd_matrix* W, const void* x, int32_t x_dtype,
   return gemv_gather_launch(*W, x, x_dtype, n_rows, cand, n_cand, max_cand, y, (hipStream_t)stream, err);
 }
 
+pkd_status rms_norm_factor(const float* x, int32_t n_rows, int32_t cols, float eps, float* inv_rms, void* x_bf16,
+                           pkd_stream stream, pkd_error* err) {
+  if (n_rows < 0) return fail(err, PKD_ERR_INVALID_ARG, n_rows, 0, "negative row count");
+  if (cols < 4 || cols % 4) return fail(err, PKD_ERR_UNSUPPORTED, cols, 4, "cols must be a positive multiple of 4");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "eps must be finite and >= 0");
+  if (n_rows == 0) return ok(err);
+  if (!x || !inv_rms) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "x or inv_rms is NULL");
+  if (!aligned16(x) || !aligned16(x_bf16) || ((uintptr_t)inv_rms & 3))
+    return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "x and x_bf16 must be 16-byte aligned, inv_rms 4-byte");
+  return rms_factor_launch(x, n_rows, cols, eps, inv_rms, x_bf16, (hipStream_t)stream, err);
+}
+
+pkd_status rope_table(const int32_t* pos, int32_t n_rows, int32_t head_dim, float base, float* cs, pkd_stream stream,
+                      pkd_error* err) {
+  if (n_rows < 0) return fail(err, PKD_ERR_INVALID_ARG, n_rows, 0, "negative row count");
+  if (head_dim < 2 || head_dim % 2) return fail(err, PKD_ERR_INVALID_ARG, head_dim, 2, "head_dim must be even");
+  if (!(base > 0.f) || !isfinite(base)) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "base must be finite and > 0");
+  if (n_rows == 0) return ok(err);
+  if (!pos || !cs) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "pos or cs is NULL");
+  if (((uintptr_t)pos & 3) || ((uintptr_t)cs & 7))
+    return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "pos must be 4-byte and cs 8-byte aligned");
+  return rope_table_launch(pos, n_rows, head_dim, base, cs, (hipStream_t)stream, err);
+}
+
 // ------------------------------------------------------------------ decode step
 struct StepWs {
   void* x_in;   // [n][D] bf16 (bf16 tier)
@@ -396,6 +434,9 @@ struct StepWs {
   size_t attn_ws_bytes;
   void* proj_ws;
   size_t proj_ws_bytes;
+  float* inv_x;  // [n] norm factor of x (PKD_LAYER_NORM)
+  float* inv_h;  // [n] norm factor of h
+  float* cs;     // [n][d / 2][2] rotary table (PKD_LAYER_ROPE)
 };
 
 static size_t step_carve(const pkd_layer* L, const pkd_pool* pool, int32_t n, uint8_t* base, StepWs* w) {
@@ -426,6 +467,11 @@ static size_t step_carve(const pkd_layer* L, const pkd_pool* pool, int32_t n, ui
   }
   t.proj_ws_bytes = pw;
   t.proj_ws = pw ? take(pw) : nullptr;
+  if (L->flags & PKD_LAYER_NORM) {
+    t.inv_x = (float*)take((size_t)n * 4);
+    t.inv_h = (float*)take((size_t)n * 4);
+  }
+  if (L->flags & PKD_LAYER_ROPE) t.cs = (float*)take((size_t)n * L->head_dim * 4);
   if (w) *w = t;
   return off;
 }
@@ -455,6 +501,12 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
     return fail(err, PKD_ERR_UNSUPPORTED, L->act_dtype, pd.kv_dtype, "an f32 layer needs an f32 pool and vice versa");
   if (L->hidden < 64 || L->hidden % 64 || L->ffn < 0 || L->ffn % 64)
     return fail(err, PKD_ERR_UNSUPPORTED, L->hidden, 64, "hidden and ffn must be multiples of 64");
+  if (L->flags & ~(PKD_LAYER_NORM | PKD_LAYER_ROPE))
+    return fail(err, PKD_ERR_INVALID_ARG, L->flags, PKD_LAYER_NORM | PKD_LAYER_ROPE, "unknown layer flags");
+  if ((L->flags & PKD_LAYER_NORM) && (!(L->norm_eps >= 0.f) || !isfinite(L->norm_eps)))
+    return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "norm_eps must be finite and >= 0");
+  if ((L->flags & PKD_LAYER_ROPE) && (!(L->rope_base > 0.f) || !isfinite(L->rope_base)))
+    return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "rope_base must be finite and > 0");
   const int D = L->hidden, d = L->head_dim, nq = L->n_q_heads, nkv = L->n_kv_heads, F = L->ffn;
   const int nqkv = (nq + 2 * nkv) * d;
   pkd_status s;
@@ -513,9 +565,16 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   }
   hipStream_t st = (hipStream_t)stream;
   if (n == 0) return ok(err);
-  // 1. qkv = W_qkv x
+  // 1. qkv = W_qkv x  (norm: W_qkv carries the gain, outputs times 1/rms(x);
+  //    rope: the q and k heads rotated by the row's position)
+  const bool norm = (L->flags & PKD_LAYER_NORM) != 0, rope = (L->flags & PKD_LAYER_ROPE) != 0;
   const bool need_cast = bf && !(L->w_qkv.family != PKD_FAMILY_GEMV && L->w_qkv.dtype == PKD_FP8_E4M3);
-  if (need_cast && (s = cast_bf16_launch(x, w.x_in, (int64_t)n * D, st, err))) return s;
+  if (norm) {
+    if ((s = rms_factor_launch(x, n, D, L->norm_eps, w.inv_x, need_cast ? w.x_in : nullptr, st, err))) return s;
+  } else if (need_cast && (s = cast_bf16_launch(x, w.x_in, (int64_t)n * D, st, err))) {
+    return s;
+  }
+  if (rope && (s = rope_table_launch(rows->pos, n, d, L->rope_base, w.cs, st, err))) return s;
   auto in0 = proj_in(L->w_qkv, x, w.x_in);
   p = ProjArgs{};
   p.W = &L->w_qkv;
@@ -524,6 +583,10 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   p.n_rows = n;
   p.y = w.qkv;
   p.out_dtype = act;
+  p.row_scale = norm ? w.inv_x : nullptr;
+  p.rope_cs = rope ? w.cs : nullptr;
+  p.rope_cols = (nq + nkv) * d;
+  p.rope_hd = d;
   if ((s = proj_launch(p, w.proj_ws, w.proj_ws_bytes, st, err))) return s;
   // 2-3. append own k, v; attention over 0..pos
   AttnArgs a{};
@@ -557,7 +620,9 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   p.y_bf16 = need_h_bf16 ? w.h_in : nullptr;
   if ((s = proj_launch(p, w.proj_ws, w.proj_ws_bytes, st, err))) return s;
   if (F == 0) return ok(err);
-  // 5. a = silu(W_gate h) * (W_up h)
+  // 5. a = silu(W_gate h) * (W_up h)  (norm: gain in W_gate_up, both halves
+  //    times 1/rms(h) before the silu)
+  if (norm && (s = rms_factor_launch(w.h, n, D, L->norm_eps, w.inv_h, nullptr, st, err))) return s;
   auto in2 = proj_in(L->w_gate_up, w.h, w.h_in);
   p = ProjArgs{};
   p.W = &L->w_gate_up;
@@ -567,6 +632,7 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   p.y = w.a;
   p.out_dtype = act;
   p.silu_pair = 1;
+  p.row_scale = norm ? w.inv_h : nullptr;
   if ((s = proj_launch(p, w.proj_ws, w.proj_ws_bytes, st, err))) return s;
   // 6. y = h + W_down a
   p = ProjArgs{};

@@ -127,6 +127,10 @@ struct ProjArgs {
   const float* residual;
   int32_t silu_pair;
   void* y_bf16;
+  const float* row_scale;  // [n_rows] factor on every output of the row, or null
+  const float* rope_cs;    // [n_rows][rope_hd / 2] (cos, sin), or null
+  int32_t rope_cols;       // outputs [0, rope_cols) are rotated in consecutive pairs
+  int32_t rope_hd;
 };
 size_t proj_workspace_bytes(const pkd_matrix* W, int32_t max_rows);
 int suggest_k_splits(int rows, int cols, int family, int typical_rows);
@@ -138,5 +142,22 @@ pkd_status gemv_gather_launch(const pkd_matrix& W, const void* x, int32_t x_dtyp
 
 // Elementwise f32 -> bf16 rounding of n values (projection inputs).
 pkd_status cast_bf16_launch(const float* x, void* y, int64_t n, hipStream_t stream, pkd_error* err);
+
+// Per-row RMSNorm factor 1 / sqrt(mean(x^2) + eps) (and optionally the bf16
+// rounding of the row), and the rotary-position table of a set of rows.
+pkd_status rms_factor_launch(const float* x, int32_t n_rows, int32_t cols, float eps, float* inv_rms,
+                             void* x_bf16, hipStream_t stream, pkd_error* err);
+pkd_status rope_table_launch(const int32_t* pos, int32_t n_rows, int32_t head_dim, float base, float* cs,
+                             hipStream_t stream, pkd_error* err);
+
+// Rotary positions on the consecutive output pair (v0, v1) at column n (even)
+// of activation row m, from the row's (cos, sin) table.  Written with explicit
+// fused multiply-adds so that every kernel that calls it rounds alike.
+__device__ __forceinline__ void rope_pair(const float* cs, int hd, int m, int n, float& v0, float& v1) {
+  const float* t = cs + ((int64_t)m * (hd / 2) + (n % hd) / 2) * 2;
+  const float c = t[0], sn = t[1], a = v0, b = v1;
+  v0 = fmaf(a, c, -(b * sn));
+  v1 = fmaf(a, sn, b * c);
+}
 
 }  // namespace pkd

@@ -49,7 +49,27 @@ struct GemmParams {
   int32_t tiles_m;
   int32_t splits;
   float* partial;  // splits > 1: [splits][M][N] raw fp32 sums
+  const float* row_scale;  // optional per-row factor (a norm's 1/rms)
+  const float* rope_cs;    // optional rotary table [M][rope_hd / 2][2]
+  int32_t rope_cols;
+  int32_t rope_hd;
 };
+
+// Epilogue shared by the single-pass kernel and the split-K finish: scale,
+// per-row factor, and (ROPE) rotary pairs on four consecutive outputs
+// n .. n + 3, n a multiple of 4.
+template <bool ROPE>
+__device__ __forceinline__ f32x4_t proj_scale4(const GemmParams& P, f32x4_t acc, float rs, int m, int n) {
+  f32x4_t v = acc * rs;
+  if (P.row_scale) v *= P.row_scale[m];
+  if (ROPE && P.rope_cs && n < P.rope_cols) {
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    rope_pair(P.rope_cs, P.rope_hd, m, n, a0, a1);
+    rope_pair(P.rope_cs, P.rope_hd, m, n + 2, a2, a3);
+    v = f32x4_t{a0, a1, a2, a3};
+  }
+  return v;
+}
 
 constexpr int TN = 256;  // weight rows per tile
 constexpr int NWAVES = 8;
@@ -449,7 +469,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       for (int a = 0; a < WA; ++a) {
         const int n = n0 + wn * WN + 16 * a + 4 * grp;
         if (n >= P.N) continue;
-        f32x4_t v = acc[a][c] * rs;
+        f32x4_t v = proj_scale4<true>(P, acc[a][c], rs, m, n);
         if (P.residual) v += *reinterpret_cast<const f32x4_t*>(P.residual + (int64_t)m * P.n_out + n);
         if (P.y_bf16) {
           uint16_t* o = reinterpret_cast<uint16_t*>(P.y) + (int64_t)m * P.y_stride + n;
@@ -465,7 +485,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       for (int a = 0; a < WA / 2; ++a) {
         const int j = n0 / 2 + wn * (WN / 2) + 16 * a + 4 * grp;
         if (j >= P.n_out) continue;
-        const f32x4_t g = acc[a][c] * rs, u = acc[a + WA / 2][c] * rs;
+        const f32x4_t g = proj_scale4<false>(P, acc[a][c], rs, m, 0),
+                      u = proj_scale4<false>(P, acc[a + WA / 2][c], rs, m, 0);
         f32x4_t v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = g[i] / (1.0f + __expf(-g[i])) * u[i];
@@ -502,11 +523,11 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams P) {
   }
   f32x4_t v;
   if (P.silu) {
-    const f32x4_t g = s * rs, u = su * rs;
+    const f32x4_t g = proj_scale4<false>(P, s, rs, m, 0), u = proj_scale4<false>(P, su, rs, m, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = g[i] / (1.0f + __expf(-g[i])) * u[i];
   } else {
-    v = s * rs;
+    v = proj_scale4<true>(P, s, rs, m, n);
     if (P.residual) v += *reinterpret_cast<const f32x4_t*>(P.residual + (int64_t)m * P.n_out + n);
   }
   if (P.y_bf16) {
@@ -625,6 +646,10 @@ pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t
   P.y_stride = P.n_out;
   P.residual = a.residual;
   P.y2 = (uint16_t*)a.y_bf16;
+  P.row_scale = a.row_scale;
+  P.rope_cs = a.rope_cs;
+  P.rope_cols = a.rope_cols;
+  P.rope_hd = a.rope_hd;
   P.tiles_n = (W.rows + TN - 1) / TN;
   P.splits = splits_of(a.W);
   const int tile_m = tile_m_for(P.tiles_n, P.splits, a.n_rows);

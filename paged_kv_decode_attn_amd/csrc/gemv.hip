@@ -37,6 +37,10 @@ struct GemvParams {
   const float* residual;
   uint16_t* y2;  // optional bf16 copy
   int32_t n_out;  // outputs per activation row (rows, or rows / 2 with silu)
+  const float* row_scale;  // optional per-row factor (a norm's 1/rms)
+  const float* rope_cs;    // optional rotary table [n_rows][rope_hd / 2][2]
+  int32_t rope_cols;
+  int32_t rope_hd;
   // Gathered rows: activation row r evaluates only the weight rows
   // cand[r][0 .. n_cand[r]) (y is then [n_rows][max_cand] f32).
   const int32_t* cand;
@@ -256,15 +260,32 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
     }
     return;
   }
+  const float rsc = P.row_scale ? P.row_scale[r] : 1.0f;
+  float vo[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if constexpr (SILU) {
+      float g = acc[i][0] * P.w_scale, u = acc[NP + i][0] * P.w_scale;
+      if (P.row_scale) { g *= rsc; u *= rsc; }
+      vo[i] = silu(g) * u;
+    } else {
+      vo[i] = acc[i][0] * P.w_scale;
+      if (P.row_scale) vo[i] *= rsc;
+    }
+  }
+  if constexpr (!SILU && NP % 2 == 0) {
+    // rotary pairs: o0 is a multiple of 4 and rope_cols of the head width
+    if (P.rope_cs && o0 < P.rope_cols) {
+#pragma unroll
+      for (int i = 0; i < NP; i += 2) rope_pair(P.rope_cs, P.rope_hd, r, o0 + i, vo[i], vo[i + 1]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int o = o0 + i;
     if (o >= P.n_out) break;
-    float v;
-    if constexpr (SILU) {
-      v = silu(acc[i][0] * P.w_scale) * (acc[NP + i][0] * P.w_scale);
-    } else {
-      v = acc[i][0] * P.w_scale;
+    float v = vo[i];
+    if constexpr (!SILU) {
       if (P.residual) v += P.residual[(int64_t)r * P.n_out + o];
     }
     if (P.y_bf16) reinterpret_cast<uint16_t*>(P.y)[(int64_t)r * P.y_stride + o] = (uint16_t)f32_to_bf16_bits(v);
@@ -368,6 +389,10 @@ pkd_status gemv_launch(const ProjArgs& a, hipStream_t stream, pkd_error* err) {
   P.y_stride = P.n_out;
   P.residual = a.residual;
   P.y2 = (uint16_t*)a.y_bf16;
+  P.row_scale = a.row_scale;
+  P.rope_cs = a.rope_cs;
+  P.rope_cols = a.rope_cols;
+  P.rope_hd = a.rope_hd;
   const bool silu = a.silu_pair != 0;
   if (W.dtype == PKD_F32) launch_w<0>(P, a.x_dtype, silu, stream);
   else if (W.dtype == PKD_BF16) launch_w<1>(P, a.x_dtype, silu, stream);

@@ -107,8 +107,10 @@ class GpuLayer:
                 return pkd.pkd_matrix()
             S = pkd.pkd_suggest_k_splits(rows, cols, fam, batch_hint) if batch_hint else 1
             return pkd.make_matrix(self.tensors[name], rows, cols, w.w_dtype, w.scales.get(name, 1.0), fam, S)
+        flags = (pkd.LAYER_NORM if w.norm else 0) | (pkd.LAYER_ROPE if w.rope else 0)
         self.layer = pkd.pkd_layer(D, nq, nkv, d, F, M("w_qkv", nqkv, D), M("w_o", D, nq * d),
-                                   M("w_gu", 2 * F, D), M("w_d", D, F), w.act_dtype)
+                                   M("w_gu", 2 * F, D), M("w_d", D, F), w.act_dtype, flags, w.norm_eps,
+                                   w.rope_base)
 
     def step(self, pool: GpuPool, seq, pos, x: torch.Tensor, ws: torch.Tensor | None = None):
         s, p = rows_tensors(seq, pos)

@@ -299,3 +299,97 @@ def test_gather_full_vocabulary_head(H, orc):
     e = H.rel_err(got[rs], want)
     print(f"full head n={n}: {e:.2e}")
     assert e <= TOL
+
+
+# ----------------------------------------------------------------------------- norm factor, rotary table, epilogue
+def test_rms_norm_factor(H, orc):
+    """1/rms per row against the oracle (fp32 sum of squares: 1e-6), the bf16
+    copy bit-exact (round to nearest even), a row's factor independent of the
+    batch, and zero rows give 1/sqrt(eps)."""
+    import paged_kv_decode_attn_amd as pkd
+    g = torch.Generator().manual_seed(40)
+    n, cols = 300, 3584
+    x = torch.randn((n, cols), generator=g) * 3.0
+    x[7] = 0.0
+    xd = x.cuda()
+    inv = torch.empty(n, device="cuda")
+    xb = torch.empty((n, cols), dtype=torch.int16, device="cuda")
+    pkd.rms_norm_factor(xd, n, cols, 1e-6, inv, xb)
+    torch.cuda.synchronize()
+    want = orc.inv_rms_rows(x.numpy().astype(np.float64), 1e-6)
+    got = inv.cpu().numpy().astype(np.float64)
+    assert np.abs(got / want - 1).max() < 1e-6
+    assert got[7] == np.float32(1 / np.sqrt(np.float32(1e-6)))
+    assert torch.equal(xb.cpu(), wl.encode(x, wl.BF16))
+    for r0, k in [(0, 1), (5, 3), (299, 1)]:
+        part = torch.empty(k, device="cuda")
+        pkd.rms_norm_factor(xd[r0:r0 + k].contiguous(), k, cols, 1e-6, part)
+        torch.cuda.synchronize()
+        assert torch.equal(part.cpu(), inv.cpu()[r0:r0 + k])
+
+
+def test_rope_table(H):
+    """(cos, sin) of pos * base^(-2i/d) within one fp32 rounding of the fp64 values."""
+    import paged_kv_decode_attn_amd as pkd
+    pos = np.array([0, 1, 31, 32, 1000, 2661, 4095, 70000], np.int32)
+    for d, base in [(128, 10000.0), (64, 500000.0)]:
+        cs = torch.empty((len(pos), d // 2, 2), device="cuda")
+        pkd.rope_table(torch.from_numpy(pos).cuda(), len(pos), d, base, cs)
+        torch.cuda.synchronize()
+        th = pos[:, None].astype(np.float64) * base ** (-np.arange(d // 2) * 2.0 / d)
+        got = cs.cpu().numpy().astype(np.float64)
+        assert np.abs(got[..., 0] - np.cos(th)).max() <= 6e-8
+        assert np.abs(got[..., 1] - np.sin(th)).max() <= 6e-8
+        assert (got[0, :, 0] == 1).all() and (got[0, :, 1] == 0).all()
+
+
+EPI_CASES = [
+    # (family, w dtype, x dtype, rows, cols, n, k splits, silu)
+    (0, wl.BF16, wl.BF16, 768, 1024, 5, 1, False),
+    (0, wl.F32, wl.F32, 768, 256, 3, 1, False),
+    (0, wl.BF16, wl.BF16, 2 * 256, 1024, 9, 1, True),
+    (1, wl.BF16, wl.BF16, 768, 1024, 130, 1, False),
+    (1, wl.BF16, wl.BF16, 768, 2048, 70, 2, False),
+    (1, wl.FP8, wl.BF16, 768, 1024, 33, 1, False),
+    (1, wl.BF16, wl.BF16, 2 * 256, 1024, 90, 3, True),
+    (2, wl.FP8, wl.F32, 768, 1024, 40, 1, False),
+]
+
+
+@pytest.mark.parametrize("fam,wdt,xdt,rows,cols,n,S,silu", EPI_CASES)
+def test_epilogue_row_scale_and_rope(H, orc, fam, wdt, xdt, rows, cols, n, S, silu):
+    """Projection epilogue with a per-row factor and (without silu) rotary
+    pairs on the first 512 outputs (four heads of 128): against the oracle's
+    matvec times the factor, rotated by the oracle's RoPE."""
+    import paged_kv_decode_attn_amd as pkd
+    seed = rows + cols + n + fam
+    W, s = make_w(rows, cols, wdt, seed)
+    x = make_x(n, cols, xdt, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    rsc = (0.5 + torch.rand(n, generator=g)).float()
+    pos = torch.randint(0, 3000, (n,), generator=g, dtype=torch.int32)
+    hd, rcols = 128, 0 if silu else 512
+    Wd = W.cuda()
+    M = pkd.make_matrix(Wd, rows, cols, wdt, s, fam, S)
+    cs = torch.empty((n, hd // 2, 2), device="cuda")
+    pkd.rope_table(pos.cuda(), n, hd, 10000.0, cs)
+    nout = rows // 2 if silu else rows
+    y = torch.empty((n, nout), device="cuda")
+    wsb = pkd.pkd_gemv_workspace_bytes(M, n)
+    pkd.gemv_rows(M, x.cuda(), xdt, n, y, wl.F32, None, silu, None, H.aligned_empty(wsb) if wsb else None,
+                  row_scale=rsc.cuda(), rope_cs=None if silu else cs, rope_cols=rcols, rope_head_dim=hd)
+    torch.cuda.synchronize()
+    if fam == 1 and wdt == wl.FP8 or fam == 2:
+        raw = oracle_proj(orc, W, wdt, s, x, xdt, 1)
+    else:
+        raw = oracle_proj(orc, W, wdt, s, x, xdt, 0)
+    raw = raw * rsc.numpy().astype(np.float64)[:, None]
+    if silu:
+        F = rows // 2
+        want = raw[:, :F] / (1 + np.exp(-raw[:, :F])) * raw[:, F:]
+    else:
+        want = raw.copy()
+        want[:, :rcols] = orc.rope_rows(raw[:, :rcols], rcols // hd, hd, pos.numpy(), 10000.0)
+    e = H.rel_err(y.cpu().numpy(), want)
+    print(f"epilogue fam{fam} w{wdt} {rows}x{cols} n={n} S={S} silu={silu}: {e:.2e}")
+    assert e <= TOL

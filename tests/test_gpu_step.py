@@ -182,6 +182,57 @@ def test_fp8_small(H, orc):
     check(H, y[rows], want["y"], BAR_FP8, "7b-fp8 small y")
 
 
+NORM_ROPE_CASES = [
+    ("tiny-f32", {}, GATE_F32),
+    ("0.6b-mixed-bf16", dict(n_decode=48, chunk_rows=24, chunk=4, long_max=1400), BAR_BF16),
+    ("0.6b-mixed-bf16", dict(n_decode=48, chunk_rows=24, chunk=4, long_max=1400, family=wl.MFMA), BAR_BF16),
+    ("7b-b4096-fp8", dict(n=64, L=100), BAR_FP8),
+]
+
+
+@pytest.mark.parametrize("name,kw,bar", NORM_ROPE_CASES)
+def test_norm_rope_step_parity(H, orc, name, kw, bar):
+    """The step with both norms (1/rms applied in the projection epilogues) and
+    rotary positions on q and k (rotated in the QKV epilogue, stored rotated)
+    against the oracle, every row, and the stored q/k/v the attention used."""
+    w = wl.with_norm_rope(wl.make(name, "cpu", **kw))
+    print(f"workload {w.name} rows={w.n_rows}", flush=True)
+    pool = H.GpuPool(w)
+    layer = H.GpuLayer(w, batch_hint=w.n_rows if w.family == wl.MFMA else None)
+    y = layer.step(pool, w.seq, w.pos, w.x).cpu().numpy()
+    want = oracle_rows(orc, w, np.arange(w.n_rows))
+    check(H, y, want["y"], bar, f"{w.name} y")
+
+
+@pytest.mark.parametrize("family", [wl.GEMV, wl.MFMA])
+def test_norm_rope_batch_invariance(H, family):
+    """With norms and rotary positions: a row alone gives its bits in the batch,
+    the prefill slice one row at a time gives the bits of the slice as one step."""
+    w = wl.with_norm_rope(wl.make("0.6b-mixed-bf16", "cpu", n_decode=24, chunk_rows=12, chunk=4, long_max=1400,
+                                  family=family))
+    layer = H.GpuLayer(w, batch_hint=8 if family == wl.MFMA else None)
+    full = layer.step(H.GpuPool(w), w.seq, w.pos, w.x).cpu()
+    for r in (0, 9, 23):
+        one = layer.step(H.GpuPool(w), w.seq[r:r + 1], w.pos[r:r + 1], w.x[r:r + 1]).cpu()
+        assert torch.equal(one[0], full[r]), r
+    pool = H.GpuPool(w)
+    for r in np.nonzero(w.seq == w.seq.max())[0]:
+        one = layer.step(pool, w.seq[r:r + 1], w.pos[r:r + 1], w.x[r:r + 1]).cpu()
+        assert torch.equal(one[0], full[r]), r
+
+
+@pytest.mark.slow
+def test_7b_b768_norm_rope(H, orc):
+    w = wl.with_norm_rope(wl.make("7b-b768-prefix-bf16", "cuda"))
+    print(f"workload {w.name}", flush=True)
+    pool = H.GpuPool(w)
+    layer = H.GpuLayer(w, batch_hint=w.n_rows)
+    y = layer.step(pool, w.seq, w.pos, w.x).cpu().numpy()
+    rows = _sample(w, 10, seed=3)
+    want = oracle_rows(orc, w, rows)
+    check(H, y[rows], want["y"], BAR_BF16, f"{w.name} (sampled rows) y")
+
+
 def _stage_inputs(w, orc, rows):
     out = oracle_rows(orc, w, rows)
     return out
@@ -239,17 +290,20 @@ def test_stage_parity(H, orc, name, kw, bar):
         assert e[k] <= bar, k
 
 
-@pytest.mark.parametrize("name,kw,hint", [
-    ("0.6b-mixed-bf16", dict(n_decode=24, chunk_rows=12, chunk=4, long_max=1400), 8),
-    ("7b-b4096-fp8", dict(n=64, L=100), 64),
+@pytest.mark.parametrize("name,kw,hint,norm_rope", [
+    ("0.6b-mixed-bf16", dict(n_decode=24, chunk_rows=12, chunk=4, long_max=1400), 8, False),
+    ("7b-b4096-fp8", dict(n=64, L=100), 64, False),
+    ("0.6b-mixed-bf16", dict(n_decode=24, chunk_rows=12, chunk=4, long_max=1400), 8, True),
 ])
-def test_step_graph_replay(H, name, kw, hint):
+def test_step_graph_replay(H, name, kw, hint, norm_rope):
     """decode_step captured in a graph and replayed several times, with eager
     work and synchronisation between replays, gives the eager result every
     time (chunked attention with its plan and merge kernels, K-split
     projections with their finish kernels, fp8 activation quantisation)."""
     import paged_kv_decode_attn_amd as pkd
     w = wl.make(name, "cpu", **kw)
+    if norm_rope:
+        w = wl.with_norm_rope(w)
     layer = H.GpuLayer(w, batch_hint=hint)
     pool = H.GpuPool(w)
     s_t, p_t = H.rows_tensors(w.seq, w.pos)

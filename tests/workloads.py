@@ -156,6 +156,10 @@ class Workload:
     k_new: torch.Tensor | None = None
     v_new: torch.Tensor | None = None
     notes: str = ""
+    norm: bool = False        # RMSNorm before attention and FFN (gains folded into the weights)
+    rope: bool = False        # rotary positions on q and k
+    norm_eps: float = 1e-6
+    rope_base: float = 10000.0
 
     @property
     def n_rows(self) -> int:
@@ -412,7 +416,20 @@ def layer_dict(w: Workload) -> dict:
                 s_qkv=w.scales.get("w_qkv", 1.0), s_o=w.scales.get("w_o", 1.0),
                 s_gu=w.scales.get("w_gu", 1.0), s_d=w.scales.get("w_d", 1.0),
                 act_dtype=w.act_dtype, act_fp8=w.act_fp8, kv_dtype=w.kv_dtype,
-                k_scale=w.k_scale, v_scale=w.v_scale)
+                k_scale=w.k_scale, v_scale=w.v_scale, norm=w.norm, rope=w.rope,
+                norm_eps=w.norm_eps, rope_base=w.rope_base)
+
+
+def with_norm_rope(w: Workload, x_std: float = 3.0) -> Workload:
+    """The same workload with both norms and rotary positions switched on.
+    The weights stand for weights with the norm gains already folded in (a
+    random gain times a random weight is another random weight), and x is
+    rescaled to standard deviation x_std so that 1/rms is far from 1."""
+    w.norm = True
+    w.rope = True
+    w.x = w.x * x_std
+    w.name += "+norm+rope"
+    return w
 
 
 def history_lists(w: Workload, seqs=None):
