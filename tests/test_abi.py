@@ -168,3 +168,25 @@ def test_gather_refusals_are_typed(pkd):
     W = pkd.pkd_matrix(1 << 20, 1000, 256, pkd.BF16, 1.0, pkd.FAMILY_GEMV)
     assert L.gemv_gather_rows(ctypes.byref(W), None, pkd.BF16, 0, None, None, 0, None, None,
                               ctypes.byref(err)) == 0  # nothing to do
+
+
+def test_norm_rope_refusals_are_typed(pkd):
+    """Host-side refusals of the norm factor, the rotary table and the
+    epilogue's rotation fields."""
+    err = pkd.pkd_error()
+    L = pkd.lib()
+    assert L.rms_norm_factor(1 << 20, 4, 102, 1e-6, 1 << 21, None, None, ctypes.byref(err)) == 2  # cols % 4
+    assert L.rms_norm_factor(1 << 20, 4, 128, -1.0, 1 << 21, None, None, ctypes.byref(err)) == 1  # eps < 0
+    assert L.rms_norm_factor(None, 4, 128, 1e-6, 1 << 21, None, None, ctypes.byref(err)) == 1
+    assert L.rms_norm_factor((1 << 20) + 4, 4, 128, 1e-6, 1 << 21, None, None, ctypes.byref(err)) == 1
+    assert L.rms_norm_factor(None, 0, 128, 1e-6, None, None, None, ctypes.byref(err)) == 0
+    assert L.rope_table(1 << 20, 4, 127, 10000.0, 1 << 21, None, ctypes.byref(err)) == 1  # odd head_dim
+    assert L.rope_table(1 << 20, 4, 128, 0.0, 1 << 21, None, ctypes.byref(err)) == 1  # base
+    assert L.rope_table(None, 4, 128, 10000.0, 1 << 21, None, ctypes.byref(err)) == 1
+    assert L.rope_table(None, 0, 128, 10000.0, None, None, ctypes.byref(err)) == 0
+    W = pkd.pkd_matrix(1 << 20, 512, 256, pkd.BF16, 1.0, pkd.FAMILY_GEMV)
+    for rope_cols, hd, silu in [(512, 126, 0), (384, 256, 0), (1024, 128, 0), (256, 128, 1)]:
+        ep = pkd.pkd_epilogue(pkd.F32, None, silu, None, None, 1 << 22, rope_cols, hd)
+        st = L.gemv_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 1, 1 << 21, ctypes.byref(ep), None, 0, None,
+                         ctypes.byref(err))
+        assert st == 1, (rope_cols, hd, silu)
