@@ -202,6 +202,28 @@ def main():
     pkd.pkd_pool_check(pool.handle)
     print(f"[bench] decode_step graph replay {ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # The same step with both RMSNorms folded into the projections and rotary
+    # positions on q and k (same weights, standing for gain-folded ones).
+    Ln = pkd.pkd_layer.from_buffer_copy(L)
+    Ln.flags, Ln.norm_eps, Ln.rope_base = pkd.LAYER_NORM | pkd.LAYER_ROPE, 1e-6, 10000.0
+    wsn = H.aligned_empty(pkd.pkd_step_workspace_bytes(Ln, pool.handle, B))
+    with torch.cuda.stream(gstream):
+        pkd.decode_step(Ln, pool.handle, rows, x, y, wsn, stream=gstream)
+        graph_n = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_n, stream=gstream):
+            pkd.decode_step(Ln, pool.handle, rows, x, y, wsn, stream=gstream)
+        for _ in range(args.warmup):
+            graph_n.replay()
+        g0.record(gstream)
+        for _ in range(args.steps):
+            graph_n.replay()
+        g1.record(gstream)
+    torch.cuda.synchronize()
+    ms_step_nr = g0.elapsed_time(g1) / args.steps
+    pkd.pkd_pool_check(pool.handle)
+    print(f"[bench] decode_step with norm + rope, graph replay {ms_step_nr * 1e3:.1f} us", file=sys.stderr,
+          flush=True)
+
     # ---------------------------------------------------------------- per stage
     # The same kernels with the same shapes, launched stage by stage through the
     # public entry points, with events between stages on the same stream.
@@ -413,6 +435,7 @@ def main():
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "us_per_step": round(ms_step * 1e3, 2),
         "us_per_step_eager": round(ms_eager * 1e3, 2),
+        "us_per_step_norm_rope": round(ms_step_nr * 1e3, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.w_dtype], "data": "synthetic",
