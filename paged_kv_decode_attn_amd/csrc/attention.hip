@@ -63,6 +63,8 @@ struct AttnParams {
   int64_t new_stride;          // elements between rows of new_k / new_v
   float enc_k_scale;           // fp8 pool: codes = E4M3(value / scale)
   float enc_v_scale;
+  int32_t tile_rows;           // > 0: runs of rows of one sequence are read as tiles of this many rows
+  const int32_t* unit_start;   // chunked: [n_rows + 1] first scheduled unit of each row
 };
 
 // Per-KV-dtype geometry.  kvt: 0 f32, 1 bf16, 2 fp8.  NL = 16-byte loads per lane
@@ -106,14 +108,13 @@ __device__ __forceinline__ bool row_ok(const AttnParams& P, int s, int p, int co
   return e == 0;
 }
 
-// Loads the query registers (B operand of the score product) of kv head g.
+// Loads the query registers (B operand of the score product): this lane's
+// column is query head h of row r (zeros when not live).
 template <int KVT, int D>
-__device__ __forceinline__ void load_q(const AttnParams& P, int r, int g, QRegs<KVT, D>& qv,
-                                       QFRegs<KVT, D>& qf) {
+__device__ __forceinline__ void load_q_at(const AttnParams& P, int r, int h, bool live, QRegs<KVT, D>& qv,
+                                          QFRegs<KVT, D>& qf) {
   using GE = Geo<KVT, D>;
-  const int l = lane_id(), grp = l >> 4, n = l & 15;
-  const bool live = n < P.G;
-  const int h = g * P.G + (live ? n : 0);
+  const int grp = lane_id() >> 4;
   if constexpr (KVT == 0) {
     const float* q = reinterpret_cast<const float*>(P.q) + (int64_t)r * P.q_stride + (int64_t)h * D;
 #pragma unroll
@@ -133,6 +134,15 @@ __device__ __forceinline__ void load_q(const AttnParams& P, int r, int g, QRegs<
       qv[s] = live ? load16(reinterpret_cast<const uint8_t*>(q + c)) : u32x4{0, 0, 0, 0};
     }
   }
+}
+
+// The G query heads of kv head g of row r as the 16 columns.
+template <int KVT, int D>
+__device__ __forceinline__ void load_q(const AttnParams& P, int r, int g, QRegs<KVT, D>& qv,
+                                       QFRegs<KVT, D>& qf) {
+  const int n = lane_id() & 15;
+  const bool live = n < P.G;
+  load_q_at<KVT, D>(P, r, g * P.G + (live ? n : 0), live, qv, qf);
 }
 
 // Scores of one page: S[a][i] = q_n . K[16a + 4grp + i] (unscaled), a = half page.
@@ -301,6 +311,48 @@ __device__ __forceinline__ void page_softmax(const AttnParams& P, Acc<KVT, D>& A
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[a][i] = fast_exp2(s[a][i] - m_new);
+      ls += p[a][i];
+    }
+  A.l = A.l * alpha + ls;
+  A.m = m_new;
+#pragma unroll
+  for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] *= alpha;
+}
+
+// The same update when a column may have no valid token in the page, or in
+// any page so far (columns of a tile whose row ends earlier, or whose row has
+// no tokens in this chunk): a column with no valid token yet keeps m = -inf,
+// l = 0, O = 0, and a page without valid tokens leaves its state untouched.
+// Wherever page_softmax is defined (a valid token has been seen) both give the
+// same bits.
+template <int KVT, int D>
+__device__ __forceinline__ void page_softmax_masked(const AttnParams& P, Acc<KVT, D>& A, const f32x4_t (&S)[2],
+                                                    int pg, int p_row, float (&p)[2][4]) {
+  using GE = Geo<KVT, D>;
+  const int grp = lane_id() >> 4;
+  float s[2][4];
+  bool valid[2][4];
+  float mx = -INFINITY;
+  const int t0 = pg * kPage + 4 * grp;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      valid[a][i] = t0 + 16 * a + i <= p_row;
+      s[a][i] = valid[a][i] ? S[a][i] * P.qk_scale : -INFINITY;
+      mx = fmaxf(mx, s[a][i]);
+    }
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  const float m_new = fmaxf(A.m, mx);
+  const bool any = m_new != -INFINITY;
+  const float alpha = any ? fast_exp2(A.m - m_new) : 1.0f;
+  float ls = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[a][i] = valid[a][i] ? fast_exp2(s[a][i] - m_new) : 0.f;
       ls += p[a][i];
     }
   A.l = A.l * alpha + ls;
@@ -506,6 +558,25 @@ __device__ __forceinline__ void zero_heads(const AttnParams& P, int r, int g) {
   for (int mt = 0; mt < D / 16; ++mt) store_out4<D>(P, r, g * P.G + n, 16 * mt + 4 * grp, f32x4_t{0.f, 0.f, 0.f, 0.f});
 }
 
+// Tiles for prompt slices: rows [t T, t T + T) (T = P.tile_rows) form a
+// shared tile when there are at least two of them and they are one sequence
+// at consecutive positions.  Every kernel that schedules rows evaluates this
+// the same way: the per-row kernels leave such rows to attn_tile_kernel.
+__device__ __forceinline__ bool tile_shared(const AttnParams& P, int t) {
+  const int T = P.tile_rows, r0 = t * T, r1 = min(P.n_rows, r0 + T);
+  if (T <= 0 || r1 - r0 < 2) return false;
+  const int s0 = P.seq[r0], p0 = P.pos[r0];
+  bool same = true;
+  for (int r = r0 + 1; r < r1; ++r) same = same && P.seq[r] == s0 && P.pos[r] == p0 + (r - r0);
+  return same;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
 // One wave per (row, kv head); every row is a single chunk.
 //   FUSE: every sequence has one row in the launch; the wave also appends its
 //   row's token (see run_unit).
@@ -528,7 +599,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   __shared__ int meta[4][2 + ST::PAGES];  // per wave: valid, page count, first table entries
   const int wave = threadIdx.x >> 6, l = lane_id();
   const int r = blockIdx.x * 4 + wave, g = blockIdx.y;
-  const bool in_range = r < P.n_rows;
+  // rows of a shared tile are attn_tile_kernel's: treated here as absent
+  const bool in_range = r < P.n_rows && !(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows));
   const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
   int count, tab;
   row_meta(P, s, count, tab);
@@ -585,11 +657,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 // Chunked mode, step 1 (one workgroup of 1024 threads): chunk count of every
 // row, exclusive prefix sum, reset of the work counter.
 __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnParams P, int32_t* row_chunks) {
-  __shared__ int32_t part[1024];
+  __shared__ int32_t part[1024], upart[1024];
   const int t = threadIdx.x, n = P.n_rows;
   const int per = (n + 1023) / 1024;
   const int r0 = min(n, t * per), r1 = min(n, r0 + per);
-  int32_t sum = 0;
+  int32_t sum = 0, usum = 0;
   for (int r = r0; r < r1; ++r) {
     const int s = P.seq[r], p = P.pos[r];
     unsigned e = 0;
@@ -600,25 +672,34 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnParams P, int32_t* 
     else c = ((p + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages;
     row_chunks[r] = c;
     sum += c;
+    // rows of shared tiles keep their chunk records but are scheduled by the tile kernel
+    if (!(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows))) usum += c;
   }
   part[t] = sum;
+  upart[t] = usum;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
+  // Hillis-Steele inclusive scans over the 1024 partial sums
   for (int off = 1; off < 1024; off <<= 1) {
     int32_t v = t >= off ? part[t - off] : 0;
+    int32_t uv = t >= off ? upart[t - off] : 0;
     __syncthreads();
     part[t] += v;
+    upart[t] += uv;
     __syncthreads();
   }
-  int32_t run = part[t] - sum;
+  int32_t run = part[t] - sum, urun = upart[t] - usum;
   int32_t* cs = const_cast<int32_t*>(P.chunk_start);
+  int32_t* us = const_cast<int32_t*>(P.unit_start);
   for (int r = r0; r < r1; ++r) {
     cs[r] = run;
+    us[r] = urun;
     run += row_chunks[r];
+    if (!(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows))) urun += row_chunks[r];
   }
   if (t == 1023) {
     cs[n] = part[1023];
-    *const_cast<int32_t*>(P.total_units) = part[1023];
+    us[n] = upart[1023];
+    *const_cast<int32_t*>(P.total_units) = upart[1023];
     *P.counter = 0;
   }
 }
@@ -636,12 +717,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     item = __shfl(item, 0, kWave);
     if (item >= total) break;
     const int u = item / P.n_kv, g = item % P.n_kv;
+    // the row owning scheduled unit u: the last row whose first unit is <= u
+    // (rows left to the tile kernel own no units)
     int lo = 0, hi = P.n_rows;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (P.chunk_start[mid] <= u) lo = mid; else hi = mid;
+      if (P.unit_start[mid] <= u) lo = mid; else hi = mid;
     }
-    const int r = lo, c = u - P.chunk_start[r];
+    const int r = lo, c = u - P.unit_start[r];
     const int nch = P.chunk_start[r + 1] - P.chunk_start[r];
     const int s = P.seq[r], p = P.pos[r];
     const int npg = (p + kPage) / kPage;
@@ -655,7 +738,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     const float lsum = group_sum(A.l);
     if (n < P.G) {
-      const int64_t rec = ((int64_t)u * P.n_kv + g) * P.G + n;
+      const int64_t rec = ((int64_t)(P.chunk_start[r] + c) * P.n_kv + g) * P.G + n;
       if (grp == 0) {
         P.part_ml[2 * rec] = A.m;
         P.part_ml[2 * rec + 1] = lsum;
@@ -663,6 +746,132 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 #pragma unroll
       for (int mt = 0; mt < GE::NMT; ++mt)
         *reinterpret_cast<f32x4_t*>(P.part_o + rec * D + 16 * mt + 4 * grp) = A.O[mt];
+    }
+  }
+}
+
+// Shared tiles (prompt slices): one wave per (tile, page chunk, kv head).  The
+// 16 columns of each of the NB matrix-core blocks are (row, query head) pairs,
+// 16 / G rows per block, so each K and V page of the chunk is read once for the
+// whole tile instead of once per row.  Every column runs the per-row
+// arithmetic: the same pages in the same order, and the pages past its own
+// position are exact no-ops for it (no valid token: weights 0, rescale 1).  V
+// is masked past the tile's last position; the positions between a column's
+// own and the tile's last are tokens of this slice, all written before the
+// kernel runs.  So each row's output is bit-identical to the per-row kernels'.
+// CHUNKED: the pool's fixed page chunks, records for the ordered merge (rows
+// refused by the plan are its job); otherwise one chunk, and refused rows get
+// zeros and their error bits here.
+template <int KVT, int D, int NB, bool CHUNKED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_tile_kernel(AttnParams P, int n_ch) {
+  using GE = Geo<KVT, D>;
+  const int t = blockIdx.x / n_ch, c = blockIdx.x % n_ch, g = blockIdx.y;
+  if (!tile_shared(P, t)) return;
+  const int l = lane_id(), grp = l >> 4, n = l & 15;
+  const int G = P.G, RPB = 16 / G;
+  const int r0 = t * P.tile_rows;
+  const int s = P.seq[r0];
+  const bool s_ok = s >= 0 && s < P.max_seqs;
+  const int count = s_ok ? P.counts[s] : 0;
+  int rw[NB], hh[NB], pc[NB], nch[NB];
+  bool live[NB], ok[NB];
+  int pmax = -1;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int j = b * RPB + n / G;
+    rw[b] = r0 + j;
+    live[b] = n < RPB * G && j < P.tile_rows && rw[b] < P.n_rows;
+    hh[b] = g * G + n % G;
+    pc[b] = live[b] ? P.pos[rw[b]] : -1;
+    ok[b] = live[b] && s_ok && pc[b] >= 0 && pc[b] < kPage * count;
+    nch[b] = !ok[b] ? 0 : CHUNKED ? ((pc[b] + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages : 1;
+    if (ok[b]) pmax = max(pmax, pc[b]);
+  }
+  pmax = wave_max_i(pmax);
+  if constexpr (!CHUNKED) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (!live[b] || ok[b]) continue;
+      for (int mt = 0; mt < GE::NMT; ++mt) store_out4<D>(P, rw[b], hh[b], 16 * mt + 4 * grp, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      if (g == 0 && grp == 0 && n % G == 0) atomicOr(P.err, !s_ok ? kErrSeq : kErrPos);
+    }
+  }
+  if (pmax < 0) return;
+  const int npg = (pmax + kPage) / kPage;
+  const int cp = CHUNKED ? P.chunk_pages : npg;
+  const int pg0 = c * cp, pg1 = min(npg, pg0 + cp);
+  if (pg0 >= npg) return;
+  bool act[NB];
+  int prow[NB];
+  u32x4 qv[NB][GE::NQ];
+  float qf[NB][GE::NQ];
+  Acc<KVT, D> A[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    act[b] = ok[b] && c < nch[b];
+    prow[b] = act[b] ? pc[b] : -1;
+    load_q_at<KVT, D>(P, act[b] ? rw[b] : r0, hh[b], act[b], qv[b], qf[b]);
+#pragma unroll
+    for (int mt = 0; mt < GE::NMT; ++mt) A[b].O[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    A[b].m = -INFINITY;
+    A[b].l = 0.f;
+  }
+  const int32_t* trow = P.table + (int64_t)s * P.max_pages;
+  const uint8_t* base = P.pages + (uint64_t)g * 2 * P.block_bytes;
+  int win = pg0;
+  int tab = pg0 + l < pg1 ? trow[pg0 + l] : 0;
+  auto page_of = [&](int pg) {
+    if (pg - win >= kWave) {
+      win += kWave;
+      tab = win + l < pg1 ? trow[win + l] : 0;
+    }
+    return __shfl(tab, pg - win, kWave);
+  };
+  u32x4 kr[GE::NL], vr[GE::NL];
+  auto load = [&](int pg, int cc, PageRegs<KVT, D>& regs) {
+    load_block<KVT, D>(base + (uint64_t)page_of(pg) * P.page_stride + cc * P.block_bytes, regs);
+  };
+  load(pg0, 0, kr);
+  load(pg0, 1, vr);
+  for (int pg = pg0; pg < pg1; ++pg) {
+    const bool nxt = pg + 1 < pg1;
+    f32x4_t S[NB][2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) page_scores<KVT, D>(kr, qv[b], qf[b], S[b]);
+    if (nxt) load(pg + 1, 0, kr);
+    float p[NB][2][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) page_softmax_masked<KVT, D>(P, A[b], S[b], pg, prow[b], p[b]);
+    if ((pg + 1) * kPage > pmax + 1) {
+      bool valid[2][4];
+      const int t0 = pg * kPage + 4 * grp;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) valid[a][i] = t0 + 16 * a + i <= pmax;
+      mask_v<KVT, D>(vr, valid);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) page_pv<KVT, D>(vr, p[b], A[b].O);
+    if (nxt) load(pg + 1, 1, vr);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float lsum = group_sum(A[b].l);
+    if (!act[b]) continue;
+    if (nch[b] == 1) {
+      const float inv = 1.0f / lsum;
+#pragma unroll
+      for (int mt = 0; mt < GE::NMT; ++mt) store_out4<D>(P, rw[b], hh[b], 16 * mt + 4 * grp, A[b].O[mt] * inv * P.v_scale);
+    } else {
+      const int64_t rec = ((int64_t)(P.chunk_start[rw[b]] + c) * P.n_kv + g) * G + n % G;
+      if (grp == 0) {
+        P.part_ml[2 * rec] = A[b].m;
+        P.part_ml[2 * rec + 1] = lsum;
+      }
+#pragma unroll
+      for (int mt = 0; mt < GE::NMT; ++mt)
+        *reinterpret_cast<f32x4_t*>(P.part_o + rec * D + 16 * mt + 4 * grp) = A[b].O[mt];
     }
   }
 }
@@ -730,6 +939,7 @@ __global__ __launch_bounds__(64) void append_kernel(AttnParams P) {
 struct AttnWs {
   int32_t* row_chunks;
   int32_t* chunk_start;
+  int32_t* unit_start;
   int32_t* total;
   int32_t* counter;
   float* part_ml;
@@ -761,6 +971,7 @@ static size_t carve(const pkd_pool* pool, int32_t n_q_heads, int32_t rows, uint8
   AttnWs t;
   t.row_chunks = (int32_t*)take(sizeof(int32_t) * (rows + 1));
   t.chunk_start = (int32_t*)take(sizeof(int32_t) * (rows + 1));
+  t.unit_start = (int32_t*)take(sizeof(int32_t) * (rows + 1));
   t.total = (int32_t*)take(sizeof(int32_t) * 4);
   t.counter = (int32_t*)take(sizeof(int32_t) * 4);
   t.part_ml = (float*)take(sizeof(float) * 2 * units);
@@ -774,9 +985,14 @@ size_t attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t max
   return carve(pool, n_q_heads, max_rows, nullptr, nullptr);
 }
 
+// Rows per shared tile: two 16-column blocks of 16 / G rows (one block for
+// f32 pools, whose page registers are twice as large).
+static int tile_rows_for(int kvt, int G) { return (kvt == PKD_F32 ? 1 : 2) * (16 / G); }
+
 template <int KVT, int D>
-static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk,
+static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk, int n_ch,
                        hipStream_t st) {
+  constexpr int NB = KVT == 0 ? 1 : 2;
   const int units = a.n_rows * n_kv;
   const dim3 tiles((a.n_rows + 3) / 4, n_kv);  // direct mode: four rows of one kv head per workgroup
   if (!chunk && a.k_new && a.distinct) {
@@ -784,13 +1000,17 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
     return;
   }
   if (a.k_new) hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
+  const int n_tiles = P.tile_rows > 0 ? (a.n_rows + P.tile_rows - 1) / P.tile_rows : 0;
   if (!chunk) {
     hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false>), tiles, dim3(256), 0, st, P);
+    if (n_tiles) hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB, false>), dim3(n_tiles, n_kv), dim3(64), 0, st, P, 1);
     return;
   }
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, st, P, w.row_chunks);
   const int grid = 256 * 8;
   hipLaunchKernelGGL((attn_chunked_kernel<KVT, D>), dim3(grid), dim3(64), 0, st, P);
+  if (n_tiles)
+    hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB, true>), dim3(n_tiles * n_ch, n_kv), dim3(64), 0, st, P, n_ch);
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units), dim3(64), 0, st, P);
 }
 
@@ -840,14 +1060,18 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   P.enc_v_scale = d.v_scale;
   const bool ch = chunked(pool);
   const int kvt = d.kv_dtype;
+  // a pure decode batch has no two rows of one sequence: no tiles to look for
+  P.tile_rows = a.distinct ? 0 : tile_rows_for(kvt, P.G);
+  P.unit_start = w.unit_start;
+  const int n_ch = ch ? (d.max_pages_per_seq + d.attn_chunk_pages - 1) / d.attn_chunk_pages : 1;
   if (d.head_dim == 128) {
-    if (kvt == PKD_F32) launch_all<0, 128>(P, a, w, d.num_kv_heads, ch, stream);
-    else if (kvt == PKD_BF16) launch_all<1, 128>(P, a, w, d.num_kv_heads, ch, stream);
-    else launch_all<2, 128>(P, a, w, d.num_kv_heads, ch, stream);
+    if (kvt == PKD_F32) launch_all<0, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
+    else if (kvt == PKD_BF16) launch_all<1, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
+    else launch_all<2, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
   } else {
-    if (kvt == PKD_F32) launch_all<0, 64>(P, a, w, d.num_kv_heads, ch, stream);
-    else if (kvt == PKD_BF16) launch_all<1, 64>(P, a, w, d.num_kv_heads, ch, stream);
-    else launch_all<2, 64>(P, a, w, d.num_kv_heads, ch, stream);
+    if (kvt == PKD_F32) launch_all<0, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
+    else if (kvt == PKD_BF16) launch_all<1, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
+    else launch_all<2, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
   }
   return check_launch(err, "paged attention");
 }

@@ -290,3 +290,71 @@ def test_block_table_refusals(H):
     out = H.run_attention(pool, w.seq, w.pos, w.q.cuda()).cpu()
     fresh = H.run_attention(H.GpuPool(w), w.seq, w.pos, w.q.cuda()).cpu()
     assert torch.equal(out, fresh)
+
+
+PREFILL_CASES = [
+    # (kv dtype, q heads, kv heads, head dim, chunk pages): rows per shared tile = (1 or 2) x 16 / G
+    (wl.BF16, 4, 2, 128, 2),     # G 2: tiles of 16 rows, chunked pool
+    (wl.BF16, 28, 4, 128, 100),  # G 7: tiles of 4 rows, one chunk
+    (wl.FP8, 16, 8, 128, 3),     # G 2, fp8 pool, chunked
+    (wl.F32, 4, 2, 64, 2),       # f32 pool: one column block, tiles of 8 rows
+    (wl.BF16, 16, 1, 64, 100),   # G 16: tiles of 2 rows
+]
+
+
+@pytest.mark.parametrize("kvt,nq,nkv,d,chunk", PREFILL_CASES)
+def test_prefill_tiles_bit_identical(H, orc, kvt, nq, nkv, d, chunk):
+    """A prompt slice (consecutive positions of one sequence) between decode
+    rows of other sequences: its rows are read as shared tiles, each K/V page
+    once per tile.  Outputs are bit-identical to the per-row kernels (the same
+    rows afterwards, tiles off) and match the oracle; the slice starts and
+    ends off the tile grid."""
+    import paged_kv_decode_attn_amd as pkd
+    lens = (96, 40, 200, 33)
+    w = wl.make("attn", "cpu", seed=11, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens, append=True, chunk=chunk,
+                extra_pages=3)
+    gen = torch.Generator().manual_seed(12)
+    qd = wl.F32 if kvt == wl.F32 else wl.BF16
+    n_slice = 37
+    seq = np.concatenate([[1, 2], np.zeros(n_slice, np.int32), [3]]).astype(np.int32)
+    pos = np.concatenate([[39, 199], np.arange(95, 95 + n_slice), [32]]).astype(np.int32)
+    n = seq.size
+    q = wl.encode(torch.randn((n, nq, d), generator=gen), qd)
+    kn = wl.encode(torch.randn((n, nkv, d), generator=gen), qd)
+    vn = wl.encode(torch.randn((n, nkv, d), generator=gen), qd)
+    pool = H.GpuPool(w)
+    out = H.run_attention(pool, seq, pos, q.cuda(), kn.cuda(), vn.cuda()).cpu()
+    pkd.pkd_pool_check(pool.handle)
+    # tiles off: the same rows through the per-row kernels, reading the tokens appended above
+    ref = H.run_attention(pool, seq, pos, q.cuda(), None, None, distinct=True).cpu()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    want = oracle_attn(orc, w, seq, pos, q, kn, vn)
+    e = H.rel_err(out.numpy(), want)
+    print(f"prefill tiles kv{kvt} G{nq // nkv} d{d} chunk {chunk}: {e:.2e}")
+    assert e <= TOL_F32_OUT
+
+
+@pytest.mark.parametrize("chunk", [2, 100])
+def test_prefill_tile_invalid_rows(H, chunk):
+    """A shared tile whose last rows run past the pages set for the sequence:
+    those rows are zeroed and reported, the others keep their bits."""
+    import paged_kv_decode_attn_amd as pkd
+    w = wl.make("attn", "cpu", seed=13, n_q=4, n_kv=2, d=128, kv_dtype=wl.BF16, lens=(60,), append=True,
+                chunk=chunk, extra_pages=0)
+    gen = torch.Generator().manual_seed(14)
+    cap = 32 * int(w.counts[0])  # positions the table covers
+    p0 = cap - 10
+    n = 16
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(p0, p0 + n, dtype=np.int32)  # the last 6 rows are past the table
+    q = wl.encode(torch.randn((n, 4, 128), generator=gen), wl.BF16).cuda()
+    kn = wl.encode(torch.randn((n, 2, 128), generator=gen), wl.BF16).cuda()
+    vn = wl.encode(torch.randn((n, 2, 128), generator=gen), wl.BF16).cuda()
+    pool = H.GpuPool(w)
+    out = H.run_attention(pool, seq, pos, q, kn, vn).cpu()
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.pkd_pool_check(pool.handle)
+    assert ei.value.needed & 2
+    assert (out[10:].view(torch.int16) == 0).all()
+    ref = H.run_attention(pool, seq[:10], pos[:10], q[:10].contiguous(), None, None, distinct=True).cpu()
+    assert torch.equal(out[:10].view(torch.int32), ref.view(torch.int32))
