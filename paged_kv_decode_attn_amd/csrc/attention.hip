@@ -53,9 +53,7 @@ struct AttnParams {
   float qk_scale;  // log2(e) / sqrt(d) * k_scale
   float v_scale;
   int32_t chunk_pages;
-  const int32_t* chunk_start;  // chunked: [n_rows + 1] first unit of each row
-  const int32_t* total_units;  // chunked: [1]
-  int32_t* counter;            // chunked: work counter
+  int32_t max_ch;              // chunked: page chunks of the longest possible row
   float* part_ml;              // chunked: [units * n_kv * G][2]  (m, l)
   float* part_o;               // chunked: [units * n_kv * G][d]
   const void* new_k;           // [n_rows][n_kv][d] in q's dtype, or null
@@ -64,8 +62,17 @@ struct AttnParams {
   float enc_k_scale;           // fp8 pool: codes = E4M3(value / scale)
   float enc_v_scale;
   int32_t tile_rows;           // > 0: runs of rows of one sequence are read as tiles of this many rows
-  const int32_t* unit_start;   // chunked: [n_rows + 1] first scheduled unit of each row
 };
+
+// Chunk count of a row (0 for a refused row) and the record of its chunk c:
+// records are laid out per (row, chunk, kv head, query head of the group).
+__device__ __forceinline__ int row_chunks(const AttnParams& P, int s, int p) {
+  if (s < 0 || s >= P.max_seqs || p < 0 || p >= kPage * P.counts[s]) return 0;
+  return ((p + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages;
+}
+__device__ __forceinline__ int64_t rec_of(const AttnParams& P, int r, int c, int g, int n) {
+  return (((int64_t)r * P.max_ch + c) * P.n_kv + g) * P.G + n;
+}
 
 // Per-KV-dtype geometry.  kvt: 0 f32, 1 bf16, 2 fp8.  NL = 16-byte loads per lane
 // for one K (or V) block of a page.
@@ -559,13 +566,20 @@ __device__ __forceinline__ void zero_heads(const AttnParams& P, int r, int g) {
 }
 
 // Tiles for prompt slices: rows [t T, t T + T) (T = P.tile_rows) form a
-// shared tile when there are at least two of them and they are one sequence
-// at consecutive positions.  Every kernel that schedules rows evaluates this
-// the same way: the per-row kernels leave such rows to attn_tile_kernel.
+// shared tile when there are at least two of them, they are one sequence at
+// consecutive positions, and the last of them is at position kTileMinPos or
+// beyond.  Below that context the per-row kernels are faster: their redundant
+// page reads are L2 hits, and a tile has T times fewer waves (measured: a
+// 256-row slice at positions 0..255 takes 49 us tiled and 37 us per row, one
+// at 1024..1279 takes 63 and 85).  Every kernel that schedules rows evaluates
+// this the same way: the per-row kernels leave such rows to attn_tile_kernel.
+constexpr int kTileMinPos = 1024;
+
 __device__ __forceinline__ bool tile_shared(const AttnParams& P, int t) {
   const int T = P.tile_rows, r0 = t * T, r1 = min(P.n_rows, r0 + T);
   if (T <= 0 || r1 - r0 < 2) return false;
   const int s0 = P.seq[r0], p0 = P.pos[r0];
+  if (p0 + (r1 - 1 - r0) < kTileMinPos) return false;
   bool same = true;
   for (int r = r0 + 1; r < r1; ++r) same = same && P.seq[r] == s0 && P.pos[r] == p0 + (r - r0);
   return same;
@@ -654,99 +668,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   finish<KVT, D>(P, A, r, g);
 }
 
-// Chunked mode, step 1 (one workgroup of 1024 threads): chunk count of every
-// row, exclusive prefix sum, reset of the work counter.
-__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnParams P, int32_t* row_chunks) {
-  __shared__ int32_t part[1024], upart[1024];
-  const int t = threadIdx.x, n = P.n_rows;
-  const int per = (n + 1023) / 1024;
-  const int r0 = min(n, t * per), r1 = min(n, r0 + per);
-  int32_t sum = 0, usum = 0;
-  for (int r = r0; r < r1; ++r) {
-    const int s = P.seq[r], p = P.pos[r];
-    unsigned e = 0;
-    if (s < 0 || s >= P.max_seqs) e = kErrSeq;
-    else if (p < 0 || p >= kPage * P.counts[s]) e = kErrPos;
-    int32_t c = 0;
-    if (e) atomicOr(P.err, e);
-    else c = ((p + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages;
-    row_chunks[r] = c;
-    sum += c;
-    // rows of shared tiles keep their chunk records but are scheduled by the tile kernel
-    if (!(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows))) usum += c;
-  }
-  part[t] = sum;
-  upart[t] = usum;
-  __syncthreads();
-  // Hillis-Steele inclusive scans over the 1024 partial sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t v = t >= off ? part[t - off] : 0;
-    int32_t uv = t >= off ? upart[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    upart[t] += uv;
-    __syncthreads();
-  }
-  int32_t run = part[t] - sum, urun = upart[t] - usum;
-  int32_t* cs = const_cast<int32_t*>(P.chunk_start);
-  int32_t* us = const_cast<int32_t*>(P.unit_start);
-  for (int r = r0; r < r1; ++r) {
-    cs[r] = run;
-    us[r] = urun;
-    run += row_chunks[r];
-    if (!(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows))) urun += row_chunks[r];
-  }
-  if (t == 1023) {
-    cs[n] = part[1023];
-    us[n] = upart[1023];
-    *const_cast<int32_t*>(P.total_units) = upart[1023];
-    *P.counter = 0;
-  }
-}
-
-// Chunked mode, step 2: persistent waves take (row, chunk, kv head) units from a
-// counter.  A row with one chunk is finished here; others leave (m, l, O).
+// Chunked mode: one wave per (row, page chunk, kv head), four chunks of one
+// row per workgroup (grid: rows x ceil(max_ch / 4) by kv heads).  Waves past
+// the row's chunks, or whose row a shared tile covers, exit at once: the grid
+// maps units directly, with no counter to contend on.  A row with one chunk is
+// finished here; the others leave (m, l, O) at record (row, chunk) for the
+// ordered merge.  A refused row is reported here (chunk 0, kv head 0) and
+// zeroed by the merge.
 template <int KVT, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunked_kernel(AttnParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunked_kernel(AttnParams P) {
   using GE = Geo<KVT, D>;
-  const int total = *P.total_units * P.n_kv;
+  const int cw = (P.max_ch + 3) / 4;
+  const int r = blockIdx.x / cw, c = 4 * (blockIdx.x % cw) + (threadIdx.x >> 6), g = blockIdx.y;
+  if (c >= P.max_ch) return;
+  if (P.tile_rows > 0 && tile_shared(P, r / P.tile_rows)) return;
   const int l = lane_id(), grp = l >> 4, n = l & 15;
-  for (;;) {
-    int item = 0;
-    if (l == 0) item = atomicAdd(P.counter, 1);
-    item = __shfl(item, 0, kWave);
-    if (item >= total) break;
-    const int u = item / P.n_kv, g = item % P.n_kv;
-    // the row owning scheduled unit u: the last row whose first unit is <= u
-    // (rows left to the tile kernel own no units)
-    int lo = 0, hi = P.n_rows;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (P.unit_start[mid] <= u) lo = mid; else hi = mid;
+  const int s = P.seq[r], p = P.pos[r];
+  const int count = (s >= 0 && s < P.max_seqs) ? P.counts[s] : 0;
+  if (!row_ok(P, s, p, count, c == 0 && g == 0)) return;
+  const int npg = (p + kPage) / kPage;
+  const int nch = (npg + P.chunk_pages - 1) / P.chunk_pages;
+  if (c >= nch) return;
+  const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
+  const int tab = pg0 + l < pg1 ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
+  Acc<KVT, D> A;
+  run_unit<KVT, D>(P, A, r, s, p, g, pg0, pg1, tab);
+  if (nch == 1) {
+    finish<KVT, D>(P, A, r, g);
+    return;
+  }
+  const float lsum = group_sum(A.l);
+  if (n < P.G) {
+    const int64_t rec = rec_of(P, r, c, g, n);
+    if (grp == 0) {
+      P.part_ml[2 * rec] = A.m;
+      P.part_ml[2 * rec + 1] = lsum;
     }
-    const int r = lo, c = u - P.unit_start[r];
-    const int nch = P.chunk_start[r + 1] - P.chunk_start[r];
-    const int s = P.seq[r], p = P.pos[r];
-    const int npg = (p + kPage) / kPage;
-    const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
-    const int tab = pg0 + l < pg1 ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
-    Acc<KVT, D> A;
-    run_unit<KVT, D>(P, A, r, s, p, g, pg0, pg1, tab);
-    if (nch == 1) {
-      finish<KVT, D>(P, A, r, g);
-      continue;
-    }
-    const float lsum = group_sum(A.l);
-    if (n < P.G) {
-      const int64_t rec = ((int64_t)(P.chunk_start[r] + c) * P.n_kv + g) * P.G + n;
-      if (grp == 0) {
-        P.part_ml[2 * rec] = A.m;
-        P.part_ml[2 * rec + 1] = lsum;
-      }
 #pragma unroll
-      for (int mt = 0; mt < GE::NMT; ++mt)
-        *reinterpret_cast<f32x4_t*>(P.part_o + rec * D + 16 * mt + 4 * grp) = A.O[mt];
-    }
+    for (int mt = 0; mt < GE::NMT; ++mt)
+      *reinterpret_cast<f32x4_t*>(P.part_o + rec * D + 16 * mt + 4 * grp) = A.O[mt];
   }
 }
 
@@ -759,10 +719,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 // is masked past the tile's last position; the positions between a column's
 // own and the tile's last are tokens of this slice, all written before the
 // kernel runs.  So each row's output is bit-identical to the per-row kernels'.
-// CHUNKED: the pool's fixed page chunks, records for the ordered merge (rows
-// refused by the plan are its job); otherwise one chunk, and refused rows get
-// zeros and their error bits here.
-template <int KVT, int D, int NB, bool CHUNKED>
+// Used with chunked pools only (the page chunks are what give a tile's pages
+// parallelism): a row with one chunk is finished here, the others leave
+// records for the ordered merge, and a refused row is reported here and
+// zeroed by the merge.
+template <int KVT, int D, int NB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_tile_kernel(AttnParams P, int n_ch) {
   using GE = Geo<KVT, D>;
   const int t = blockIdx.x / n_ch, c = blockIdx.x % n_ch, g = blockIdx.y;
@@ -784,22 +745,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     hh[b] = g * G + n % G;
     pc[b] = live[b] ? P.pos[rw[b]] : -1;
     ok[b] = live[b] && s_ok && pc[b] >= 0 && pc[b] < kPage * count;
-    nch[b] = !ok[b] ? 0 : CHUNKED ? ((pc[b] + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages : 1;
+    nch[b] = ok[b] ? ((pc[b] + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages : 0;
     if (ok[b]) pmax = max(pmax, pc[b]);
   }
   pmax = wave_max_i(pmax);
-  if constexpr (!CHUNKED) {
+  // refused rows: reported once (chunk 0, kv head 0), zeroed by the merge
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (!live[b] || ok[b]) continue;
-      for (int mt = 0; mt < GE::NMT; ++mt) store_out4<D>(P, rw[b], hh[b], 16 * mt + 4 * grp, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      if (g == 0 && grp == 0 && n % G == 0) atomicOr(P.err, !s_ok ? kErrSeq : kErrPos);
-    }
-  }
+  for (int b = 0; b < NB; ++b)
+    if (live[b] && !ok[b] && c == 0 && g == 0 && grp == 0 && n % G == 0)
+      atomicOr(P.err, !s_ok ? kErrSeq : kErrPos);
   if (pmax < 0) return;
   const int npg = (pmax + kPage) / kPage;
-  const int cp = CHUNKED ? P.chunk_pages : npg;
-  const int pg0 = c * cp, pg1 = min(npg, pg0 + cp);
+  const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
   if (pg0 >= npg) return;
   bool act[NB];
   int prow[NB];
@@ -864,7 +821,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 #pragma unroll
       for (int mt = 0; mt < GE::NMT; ++mt) store_out4<D>(P, rw[b], hh[b], 16 * mt + 4 * grp, A[b].O[mt] * inv * P.v_scale);
     } else {
-      const int64_t rec = ((int64_t)(P.chunk_start[rw[b]] + c) * P.n_kv + g) * G + n % G;
+      const int64_t rec = rec_of(P, rw[b], c, g, n % G);
       if (grp == 0) {
         P.part_ml[2 * rec] = A[b].m;
         P.part_ml[2 * rec + 1] = lsum;
@@ -876,13 +833,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   }
 }
 
-// Chunked mode, step 3: one wave per (row, kv head) merges the chunk results
-// of rows with more than one chunk, in ascending chunk order; rows refused by
-// the plan get zeros.
+// Chunked mode, last step: one wave per (row, kv head) merges the chunk
+// results of rows with more than one chunk, in ascending chunk order; refused
+// rows get zeros.
 template <int D>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
   const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
-  const int c0 = P.chunk_start[r], nch = P.chunk_start[r + 1] - c0;
+  const int nch = row_chunks(P, P.seq[r], P.pos[r]);
   if (nch == 1) return;
   const int l = lane_id();
   constexpr int PER = D / 64;  // dims per lane
@@ -894,12 +851,12 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
       for (int j = 0; j < PER; ++j) o[j] = 0.f;
     } else {
       float M = -INFINITY;
-      for (int c = 0; c < nch; ++c) M = fmaxf(M, P.part_ml[2 * (((int64_t)(c0 + c) * P.n_kv + g) * P.G + n)]);
+      for (int c = 0; c < nch; ++c) M = fmaxf(M, P.part_ml[2 * rec_of(P, r, c, g, n)]);
       float L = 0.f;
 #pragma unroll
       for (int j = 0; j < PER; ++j) o[j] = 0.f;
       for (int c = 0; c < nch; ++c) {
-        const int64_t rec = ((int64_t)(c0 + c) * P.n_kv + g) * P.G + n;
+        const int64_t rec = rec_of(P, r, c, g, n);
         const float w = fast_exp2(P.part_ml[2 * rec] - M);
         L += P.part_ml[2 * rec + 1] * w;
 #pragma unroll
@@ -937,11 +894,6 @@ __global__ __launch_bounds__(64) void append_kernel(AttnParams P) {
 
 // ------------------------------------------------------------------ host
 struct AttnWs {
-  int32_t* row_chunks;
-  int32_t* chunk_start;
-  int32_t* unit_start;
-  int32_t* total;
-  int32_t* counter;
   float* part_ml;
   float* part_o;
 };
@@ -969,11 +921,6 @@ static size_t carve(const pkd_pool* pool, int32_t n_q_heads, int32_t rows, uint8
   const int G = n_q_heads / pool->desc.num_kv_heads;
   const size_t units = max_units(pool, rows) * pool->desc.num_kv_heads * G;
   AttnWs t;
-  t.row_chunks = (int32_t*)take(sizeof(int32_t) * (rows + 1));
-  t.chunk_start = (int32_t*)take(sizeof(int32_t) * (rows + 1));
-  t.unit_start = (int32_t*)take(sizeof(int32_t) * (rows + 1));
-  t.total = (int32_t*)take(sizeof(int32_t) * 4);
-  t.counter = (int32_t*)take(sizeof(int32_t) * 4);
   t.part_ml = (float*)take(sizeof(float) * 2 * units);
   t.part_o = (float*)take(sizeof(float) * (size_t)pool->desc.head_dim * units);
   if (w) *w = t;
@@ -1003,14 +950,11 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
   const int n_tiles = P.tile_rows > 0 ? (a.n_rows + P.tile_rows - 1) / P.tile_rows : 0;
   if (!chunk) {
     hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false>), tiles, dim3(256), 0, st, P);
-    if (n_tiles) hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB, false>), dim3(n_tiles, n_kv), dim3(64), 0, st, P, 1);
     return;
   }
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, st, P, w.row_chunks);
-  const int grid = 256 * 8;
-  hipLaunchKernelGGL((attn_chunked_kernel<KVT, D>), dim3(grid), dim3(64), 0, st, P);
+  hipLaunchKernelGGL((attn_chunked_kernel<KVT, D>), dim3(a.n_rows * ((n_ch + 3) / 4), n_kv), dim3(256), 0, st, P);
   if (n_tiles)
-    hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB, true>), dim3(n_tiles * n_ch, n_kv), dim3(64), 0, st, P, n_ch);
+    hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB>), dim3(n_tiles * n_ch, n_kv), dim3(64), 0, st, P, n_ch);
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units), dim3(64), 0, st, P);
 }
 
@@ -1048,9 +992,6 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   P.qk_scale = (float)(1.4426950408889634 / sqrt((double)d.head_dim)) * d.k_scale;
   P.v_scale = d.v_scale;
   P.chunk_pages = d.attn_chunk_pages;
-  P.chunk_start = w.chunk_start;
-  P.total_units = w.total;
-  P.counter = w.counter;
   P.part_ml = w.part_ml;
   P.part_o = w.part_o;
   P.new_k = a.k_new;
@@ -1060,10 +1001,16 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   P.enc_v_scale = d.v_scale;
   const bool ch = chunked(pool);
   const int kvt = d.kv_dtype;
-  // a pure decode batch has no two rows of one sequence: no tiles to look for
-  P.tile_rows = a.distinct ? 0 : tile_rows_for(kvt, P.G);
-  P.unit_start = w.unit_start;
   const int n_ch = ch ? (d.max_pages_per_seq + d.attn_chunk_pages - 1) / d.attn_chunk_pages : 1;
+  P.max_ch = n_ch;
+  // Shared tiles pay only where page chunks give them parallelism (with one
+  // chunk per row a tile is a single wave walking every page, slower than one
+  // wave per row) and in calls of at least kTileMinRows rows (below that the
+  // per-row kernels were faster at every measured context: the tile kernel is
+  // one more launch and gives fewer waves).  A pure decode batch has no two
+  // rows of one sequence.
+  constexpr int kTileMinRows = 128;
+  P.tile_rows = (a.distinct || !ch || a.n_rows < kTileMinRows) ? 0 : tile_rows_for(kvt, P.G);
   if (d.head_dim == 128) {
     if (kvt == PKD_F32) launch_all<0, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
     else if (kvt == PKD_BF16) launch_all<1, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);

@@ -294,11 +294,11 @@ def test_block_table_refusals(H):
 
 PREFILL_CASES = [
     # (kv dtype, q heads, kv heads, head dim, chunk pages): rows per shared tile = (1 or 2) x 16 / G
-    (wl.BF16, 4, 2, 128, 2),     # G 2: tiles of 16 rows, chunked pool
-    (wl.BF16, 28, 4, 128, 100),  # G 7: tiles of 4 rows, one chunk
-    (wl.FP8, 16, 8, 128, 3),     # G 2, fp8 pool, chunked
-    (wl.F32, 4, 2, 64, 2),       # f32 pool: one column block, tiles of 8 rows
-    (wl.BF16, 16, 1, 64, 100),   # G 16: tiles of 2 rows
+    (wl.BF16, 4, 2, 128, 2),    # G 2: tiles of 16 rows
+    (wl.BF16, 28, 4, 128, 8),   # G 7: tiles of 4 rows
+    (wl.FP8, 16, 8, 128, 3),    # G 2, fp8 pool
+    (wl.F32, 4, 2, 64, 2),      # f32 pool: one column block, tiles of 8 rows
+    (wl.BF16, 16, 1, 64, 5),    # G 16: tiles of 2 rows
 ]
 
 
@@ -310,14 +310,15 @@ def test_prefill_tiles_bit_identical(H, orc, kvt, nq, nkv, d, chunk):
     rows afterwards, tiles off) and match the oracle; the slice starts and
     ends off the tile grid."""
     import paged_kv_decode_attn_amd as pkd
-    lens = (96, 40, 200, 33)
+    lens = (1100, 40, 200, 33)
     w = wl.make("attn", "cpu", seed=11, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens, append=True, chunk=chunk,
-                extra_pages=3)
+                extra_pages=6)
     gen = torch.Generator().manual_seed(12)
     qd = wl.F32 if kvt == wl.F32 else wl.BF16
-    n_slice = 37
+    # 150 slice rows at positions 1001.. (tiles need a 128-row call and a last position >= 1024)
+    n_slice = 150
     seq = np.concatenate([[1, 2], np.zeros(n_slice, np.int32), [3]]).astype(np.int32)
-    pos = np.concatenate([[39, 199], np.arange(95, 95 + n_slice), [32]]).astype(np.int32)
+    pos = np.concatenate([[39, 199], np.arange(1001, 1001 + n_slice), [32]]).astype(np.int32)
     n = seq.size
     q = wl.encode(torch.randn((n, nq, d), generator=gen), qd)
     kn = wl.encode(torch.randn((n, nkv, d), generator=gen), qd)
@@ -334,17 +335,17 @@ def test_prefill_tiles_bit_identical(H, orc, kvt, nq, nkv, d, chunk):
     assert e <= TOL_F32_OUT
 
 
-@pytest.mark.parametrize("chunk", [2, 100])
+@pytest.mark.parametrize("chunk", [2, 5])
 def test_prefill_tile_invalid_rows(H, chunk):
     """A shared tile whose last rows run past the pages set for the sequence:
     those rows are zeroed and reported, the others keep their bits."""
     import paged_kv_decode_attn_amd as pkd
-    w = wl.make("attn", "cpu", seed=13, n_q=4, n_kv=2, d=128, kv_dtype=wl.BF16, lens=(60,), append=True,
+    w = wl.make("attn", "cpu", seed=13, n_q=4, n_kv=2, d=128, kv_dtype=wl.BF16, lens=(1100,), append=True,
                 chunk=chunk, extra_pages=0)
     gen = torch.Generator().manual_seed(14)
     cap = 32 * int(w.counts[0])  # positions the table covers
-    p0 = cap - 10
-    n = 16
+    n = 128
+    p0 = cap - 122
     seq = np.zeros(n, np.int32)
     pos = np.arange(p0, p0 + n, dtype=np.int32)  # the last 6 rows are past the table
     q = wl.encode(torch.randn((n, 4, 128), generator=gen), wl.BF16).cuda()
@@ -355,6 +356,6 @@ def test_prefill_tile_invalid_rows(H, chunk):
     with pytest.raises(pkd.PkdError) as ei:
         pkd.pkd_pool_check(pool.handle)
     assert ei.value.needed & 2
-    assert (out[10:].view(torch.int16) == 0).all()
-    ref = H.run_attention(pool, seq[:10], pos[:10], q[:10].contiguous(), None, None, distinct=True).cpu()
-    assert torch.equal(out[:10].view(torch.int32), ref.view(torch.int32))
+    assert (out[122:].view(torch.int16) == 0).all()
+    ref = H.run_attention(pool, seq[:122], pos[:122], q[:122].contiguous(), None, None, distinct=True).cpu()
+    assert torch.equal(out[:122].view(torch.int32), ref.view(torch.int32))
