@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-t2", action="store_true", help="skip the small-batch GEMV pass")
     ap.add_argument("--no-head", action="store_true", help="skip the output-head (candidate rows) pass")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-chunk (prefill) pass")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--family", type=int, default=None, help="override the projection family")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -407,6 +408,69 @@ def main():
                 del yd
             head_res[f"B{nb}"] = ent
         del Wh, Mh
+    # Prefill of one 2,662-token prompt in 256-token chunks through the same
+    # layer shape: the chunk as one step (matrix-core projections, shared-tile
+    # attention) against the same 256 tokens one step each (vector GEMV at
+    # batch 1), and the chunk's attention with shared tiles against per-row.
+    prefill_res = None
+    if not args.no_prefill and w.w_dtype == 1 and F:
+        lname = "7b" if D == 3584 else "0.6b"
+        prefill_res = {"layer": lname, "prompt_tokens": 2662, "chunk_tokens": 256, "attn_chunk_pages": 8}
+        for p0 in (1024, 2304):
+            wp = wl.make("prefill-chunk", "cuda", layer=lname, p0=p0, n=256, seed=3)
+            poolp = H.GpuPool(wp)
+            layp = H.GpuLayer(wp, batch_hint=256)
+            nP = wp.n_rows
+            sp, pp = H.rows_tensors(wp.seq, wp.pos)
+            rows_p = pkd.make_rows(sp, pp, False)
+            xp = wp.x.contiguous()
+            yp = torch.empty((nP, D), dtype=torch.float32, device="cuda")
+            wsp = H.aligned_empty(pkd.pkd_step_workspace_bytes(layp.layer, poolp.handle, nP))
+            with torch.cuda.stream(gstream):
+                pkd.decode_step(layp.layer, poolp.handle, rows_p, xp, yp, wsp, stream=gstream)
+                gp = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gp, stream=gstream):
+                    pkd.decode_step(layp.layer, poolp.handle, rows_p, xp, yp, wsp, stream=gstream)
+                for _ in range(args.warmup):
+                    gp.replay()
+                g0.record(gstream)
+                for _ in range(args.steps):
+                    gp.replay()
+                g1.record(gstream)
+            torch.cuda.synchronize()
+            us_chunk = g0.elapsed_time(g1) / args.steps * 1e3
+            pkd.pkd_pool_check(poolp.handle)
+            # the same 256 tokens one step each, in order (vector family at batch 1)
+            lay1 = H.GpuLayer(wp, family=0)
+            ws1 = H.aligned_empty(pkd.pkd_step_workspace_bytes(lay1.layer, poolp.handle, 1))
+            y1 = torch.empty((1, D), dtype=torch.float32, device="cuda")
+            one_rows = [pkd.make_rows(sp[i:i + 1], pp[i:i + 1], True) for i in range(nP)]
+            xs1 = [xp[i:i + 1] for i in range(nP)]
+
+            def token_by_token():
+                for i in range(nP):
+                    pkd.decode_step(lay1.layer, poolp.handle, one_rows[i], xs1[i], y1, ws1)
+            token_by_token()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            token_by_token()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us_tokens = e0.elapsed_time(e1) * 1e3
+            # attention of the chunk alone (appends already in the pool): shared tiles against per-row
+            qa = (torch.randn((nP, nq, d), device="cuda")).to(torch.bfloat16).view(torch.int16)
+            oa = torch.empty((nP, nq, d), dtype=torch.int16, device="cuda")
+            wsa = H.aligned_empty(pkd.pkd_attn_workspace_bytes(poolp.handle, nq, nP))
+            rows_row = pkd.make_rows(sp, pp, True)  # no append: the per-row kernels, tiles off
+            att_t, _, _ = timed(lambda: pkd.paged_attn_decode(poolp.handle, rows_p, nq, qa, None, None, oa, 1, wsa),
+                                max(args.steps, 10), False)
+            att_r, _, _ = timed(lambda: pkd.paged_attn_decode(poolp.handle, rows_row, nq, qa, None, None, oa, 1, wsa),
+                                max(args.steps, 10), False)
+            prefill_res[f"pos{p0}"] = {
+                "us_chunk_step": round(us_chunk, 1), "tokens_per_s": round(nP / us_chunk * 1e6),
+                "us_token_by_token": round(us_tokens, 1), "speedup_vs_token_by_token": round(us_tokens / us_chunk, 1),
+                "attention_us_shared_tiles": round(att_t, 2), "attention_us_per_row": round(att_r, 2)}
+            del wp, poolp, layp, lay1
     del flush, flush_sum
 
     # ---------------------------------------------------------------- CPU baseline
@@ -448,6 +512,7 @@ def main():
         "t1_attention": t1_res,
         "t2_gemv": t2_res,
         "output_head": head_res,
+        "prefill": prefill_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

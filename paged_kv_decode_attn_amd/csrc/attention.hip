@@ -833,48 +833,69 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   }
 }
 
-// Chunked mode, last step: one wave per (row, kv head) merges the chunk
-// results of rows with more than one chunk, in ascending chunk order; refused
-// rows get zeros.
+// Chunked mode, last step: one wave per (row, query head) merges the chunk
+// results of rows with more than one chunk; refused rows get zeros.  Lane c
+// holds chunk c's (m, l) (64 chunks at a time), so the maximum is one wave
+// reduction and the weights are computed in parallel; the weighted sums of l
+// and of O are then taken in ascending chunk order, with the O loads of
+// several chunks in flight at once.
 template <int D>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
-  const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
+  const int hq = P.n_kv * P.G;
+  const int r = blockIdx.x / hq, h = blockIdx.x % hq, g = h / P.G, n = h % P.G;
   const int nch = row_chunks(P, P.seq[r], P.pos[r]);
   if (nch == 1) return;
   const int l = lane_id();
   constexpr int PER = D / 64;  // dims per lane
-  for (int n = 0; n < P.G; ++n) {
-    const int h = g * P.G + n;
-    float o[PER];
-    if (nch == 0) {
+  float o[PER];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) o[j] = 0.f;
-    } else {
-      float M = -INFINITY;
-      for (int c = 0; c < nch; ++c) M = fmaxf(M, P.part_ml[2 * rec_of(P, r, c, g, n)]);
-      float L = 0.f;
+  for (int j = 0; j < PER; ++j) o[j] = 0.f;
+  if (nch > 0) {
+    float M = -INFINITY;
+    for (int c0 = 0; c0 < nch; c0 += kWave)
+      if (c0 + l < nch) M = fmaxf(M, P.part_ml[2 * rec_of(P, r, c0 + l, g, n)]);
 #pragma unroll
-      for (int j = 0; j < PER; ++j) o[j] = 0.f;
-      for (int c = 0; c < nch; ++c) {
-        const int64_t rec = rec_of(P, r, c, g, n);
-        const float w = fast_exp2(P.part_ml[2 * rec] - M);
-        L += P.part_ml[2 * rec + 1] * w;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) o[j] += P.part_o[rec * D + PER * l + j] * w;
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
+    float L = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += kWave) {
+      float wl = 0.f, ll = 0.f;
+      if (c0 + l < nch) {
+        const int64_t rec = rec_of(P, r, c0 + l, g, n);
+        wl = fast_exp2(P.part_ml[2 * rec] - M);
+        ll = P.part_ml[2 * rec + 1];
       }
-      const float inv = 1.0f / L;
+      const int cn = min(kWave, nch - c0);
+      constexpr int U = 4;
+      for (int c = 0; c < cn; c += U) {
+        float v[U][PER];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) o[j] = o[j] * inv * P.v_scale;
+        for (int u = 0; u < U; ++u) {
+          const int64_t rec = rec_of(P, r, c0 + min(c + u, cn - 1), g, n);
+#pragma unroll
+          for (int j = 0; j < PER; ++j) v[u][j] = P.part_o[rec * D + PER * l + j];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (c + u >= cn) break;
+          const float w = __shfl(wl, c + u, kWave);
+          L += __shfl(ll, c + u, kWave) * w;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) o[j] += v[u][j] * w;
+        }
+      }
     }
-    if (P.out_bf16) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + PER * l;
+    const float inv = 1.0f / L;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) dst[j] = (uint16_t)f32_to_bf16_bits(o[j]);
-    } else {
-      float* dst = reinterpret_cast<float*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + PER * l;
+    for (int j = 0; j < PER; ++j) o[j] = o[j] * inv * P.v_scale;
+  }
+  if (P.out_bf16) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + PER * l;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) dst[j] = o[j];
-    }
+    for (int j = 0; j < PER; ++j) dst[j] = (uint16_t)f32_to_bf16_bits(o[j]);
+  } else {
+    float* dst = reinterpret_cast<float*>(P.out) + (int64_t)r * P.out_stride + (int64_t)h * D + PER * l;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) dst[j] = o[j];
   }
 }
 
@@ -955,7 +976,7 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
   hipLaunchKernelGGL((attn_chunked_kernel<KVT, D>), dim3(a.n_rows * ((n_ch + 3) / 4), n_kv), dim3(256), 0, st, P);
   if (n_tiles)
     hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB>), dim3(n_tiles * n_ch, n_kv), dim3(64), 0, st, P, n_ch);
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units), dim3(64), 0, st, P);
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units * P.G), dim3(64), 0, st, P);
 }
 
 pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err) {
