@@ -255,6 +255,15 @@ size_t pkd_attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t
  *        softmax_t(q . K_t / sqrt(head_dim)) applied to V over t = 0..pos.
  * ws     device workspace of at least pkd_attn_workspace_bytes(pool, n_q_heads, n).
  * Invalid rows: see pkd_pool_check.
+ * Scheduling (results are bit-identical whichever applies): with a pool
+ * whose attn_chunk_pages covers max_pages_per_seq, one wave per (row, kv
+ * head); otherwise one wave per (row, page chunk, kv head) and an ordered
+ * merge.  On such chunked pools, in calls of at least 128 rows without
+ * PKD_ROWS_DISTINCT_SEQS, runs of consecutive rows of one sequence at
+ * consecutive positions (a prompt slice, [LRS] section 4, "Prefill: tensor
+ * cores, written by hand") whose tile ends at position 1024 or later are read
+ * as tiles of 2 x (16 / G) rows (16 / G for f32 pools), each K/V page once
+ * per tile.
  */
 pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_heads,
                              const void* q, const void* k_new, const void* v_new,
