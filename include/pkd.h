@@ -332,7 +332,7 @@ size_t pkd_gemv_workspace_bytes(const pkd_matrix* W, int32_t max_rows);
 /*
  * A k_splits value for a matrix-core matrix of rows x cols that will mostly
  * see batches of about typical_rows rows: the S in {1, 2, 3, 4, 6, 8}, with
- * at least 1536 columns per split, that minimises the estimated time at that
+ * at least 512 columns per split, that minimises the estimated time at that
  * batch (rounds of workgroups over the compute units times the K-work of one
  * workgroup; a larger S must win by 5%).  The caller fixes
  * the result in the pkd_matrix once (results depend on S, never on the batch

@@ -595,19 +595,27 @@ static int tile_m_for(int tiles_n, int splits, int M) {
 }
 
 
-// Estimated cost of a split: rounds of workgroups over the 256 CUs times the
-// work of one workgroup (tile height x its share of K).  A larger S must beat
-// the best so far by 5% to be taken (the partial sums cost a second pass).
+// Estimated time of a split, in microseconds: rounds of workgroups over the
+// 256 CUs times the time of one workgroup (tile height x 256 weight rows x its
+// share of K, at about 4 TFLOP/s per CU as measured for these tiles), plus the
+// partial sums of S > 1, written once and read once by the finish pass (at
+// about 5 TB/s).  A larger S must beat the best so far by 5%.  With these two
+// terms the model picks the measured best S at the 7B shapes at batch 768
+// (qkv 2, W_o 3, gate/up 1, down 3) and within 5% of it at batch 256 (qkv 4,
+// W_o 6, gate/up 1, down 8).
 int suggest_k_splits(int rows, int cols, int family, int typical_rows) {
   if (family == PKD_FAMILY_GEMV || rows <= 0 || cols <= 0 || typical_rows <= 0) return 1;
+  constexpr double kFlopsPerCu = 4e12, kPartialBytesPerS = 5e12;
   const int tiles_n = (rows + TN - 1) / TN;
   int best = 1;
   double best_cost = 0;
   for (int s : {1, 2, 3, 4, 6, 8}) {
-    if (s > 1 && cols / s < 1536) break;
+    if (s > 1 && cols / s < 512) break;
     const int tm = tile_m_for(tiles_n, s, typical_rows);
     const long items = (long)tiles_n * s * ((typical_rows + tm - 1) / tm);
-    const double cost = (double)((items + 255) / 256) * (tm / 128) * ((cols + s - 1) / s);
+    const double wg_us = 2.0 * tm * TN * ((cols + s - 1) / s) / kFlopsPerCu * 1e6;
+    const double partial_us = s > 1 ? 2.0 * s * rows * (double)typical_rows * 4 / kPartialBytesPerS * 1e6 : 0.0;
+    const double cost = (double)((items + 255) / 256) * wg_us + partial_us;
     if (s == 1 || cost < 0.95 * best_cost) {
       best = s;
       best_cost = cost;

@@ -131,17 +131,21 @@ def test_suggested_k_splits(pkd):
     """Host-only split policy: long-K and narrow matrices are split, a wide one
     that already fills the chip is not, the vector family never is."""
     D, F, M = 3584, 18944, 768
+    # the measured best S at these 7B shapes (batch 768: qkv 2, W_o 3, gate/up 1,
+    # down 3; batch 256: qkv 6 (4 within 5%), down 8)
     assert pkd.pkd_suggest_k_splits(4608, D, 1, M) == 2
-    assert pkd.pkd_suggest_k_splits(D, D, 1, M) == 2
+    assert pkd.pkd_suggest_k_splits(D, D, 1, M) == 3
     assert pkd.pkd_suggest_k_splits(2 * F, D, 1, M) == 1
-    assert pkd.pkd_suggest_k_splits(D, F, 1, M) >= 3
+    assert pkd.pkd_suggest_k_splits(D, F, 1, M) == 3
+    assert pkd.pkd_suggest_k_splits(4608, D, 1, 256) in (4, 6)
+    assert pkd.pkd_suggest_k_splits(D, F, 1, 256) == 8
     assert pkd.pkd_suggest_k_splits(D, F, 0, M) == 1
     assert pkd.pkd_suggest_k_splits(D, 1024, 1, M) == 1
     assert pkd.pkd_suggest_k_splits(0, D, 1, M) == 1
     for rows, cols in [(4608, D), (D, F), (2 * F, D)]:
         for m in (1, 64, 768, 4096):
             S = pkd.pkd_suggest_k_splits(rows, cols, 2, m)
-            assert S in (1, 2, 3, 4, 6, 8) and (S == 1 or cols // S >= 1536)
+            assert S in (1, 2, 3, 4, 6, 8) and (S == 1 or cols // S >= 512)
 
 
 def test_gather_refusals_are_typed(pkd):
