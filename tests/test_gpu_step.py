@@ -361,3 +361,23 @@ def test_zero_rows_are_no_ops(H):
     assert bool((y == 7.0).all()) and bool((out == 7.0).all())
     assert torch.equal(pool.pages_bytes(), before)
     pkd.pkd_pool_check(pool.handle)
+
+
+@pytest.mark.parametrize("layer", ["0.6b", pytest.param("7b", marks=pytest.mark.slow)])
+def test_prefill_chunk_step(H, orc, layer):
+    """A 256-token prompt chunk at positions 1024..1279 as one step (prompt
+    slice read as shared tiles, matrix-core projections): sampled rows
+    against the oracle, and rows run alone afterwards give the same bits."""
+    w = wl.make("prefill-chunk", "cpu", layer=layer, p0=1024, n=256, seed=4)
+    print(f"workload {w.name} rows={w.n_rows}", flush=True)
+    pool = H.GpuPool(w)
+    lay = H.GpuLayer(w, batch_hint=256)
+    y = lay.step(pool, w.seq, w.pos, w.x).cpu()
+    rows = [0, 1, 77, 128, 255]
+    # the oracle needs every row up to the sampled one (each row's token is in
+    # the history of the later ones)
+    want = oracle_rows(orc, w, np.arange(256))
+    check(H, y.numpy()[rows], want["y"][rows], BAR_BF16, f"{w.name} y")
+    for r in (0, 100, 255):
+        one = lay.step(pool, w.seq[r:r + 1], w.pos[r:r + 1], w.x[r:r + 1]).cpu()
+        assert torch.equal(one[0], y[r]), r
