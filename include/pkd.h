@@ -73,10 +73,16 @@ typedef enum {
   PKD_FAMILY_MFMA = 1,    /* tiled matrix-core contraction for large batches: bf16 operands, or
                              fp8 operands decoded exactly to bf16 on chip; products exact and
                              sums with fp32 accumulation */
-  PKD_FAMILY_MFMA_FP8 = 2 /* fp8 weights only: the native fp8 matrix-core instruction, twice the
+  PKD_FAMILY_MFMA_FP8 = 2, /* fp8 weights only: the native fp8 matrix-core instruction, twice the
                              matrix-core rate, but each instruction sums its 128 products with
                              ~17 significant bits (measured relative error of a projection
                              ~2e-5 instead of ~1e-7) */
+  PKD_FAMILY_GEMV_MFMA = 3 /* GEMV on the matrix cores for decode batches of about 8 to 16: one
+                             wave per 16 weight rows read straight into registers, the batch as
+                             the product's 16 columns; bf16 or fp8 weights (fp8 decoded exactly),
+                             bf16 activations, fp32 accumulation.  Measured on the 7B matrices:
+                             faster than PKD_FAMILY_GEMV from batch 8 (156 against 199 us at
+                             16), slower below (103 against 93 us at 1). */
 } pkd_family;
 
 /* ------------------------------------------------------------------------ */
@@ -344,6 +350,7 @@ int32_t pkd_suggest_k_splits(int32_t rows, int32_t cols, int32_t family, int32_t
 /*
  * y = epilogue(W x_r) for each of the n_rows rows of x (device [n_rows][cols]).
  *   GEMV family: x is f32 or bf16 and is used exactly; fp32 accumulation.
+ *   GEMV_MFMA family: bf16 or fp8 weights, x must be bf16; fp32 accumulation.
  *   MFMA family, bf16 weights: x must be bf16; fp32 accumulation.
  *   MFMA and MFMA_FP8 families, fp8 weights: x (f32 or bf16) is quantised per
  *     row (s = max|x| / 448 in fp32, codes = E4M3 RNE of x / s, saturating),
@@ -372,7 +379,7 @@ pkd_status gemv_rows(const pkd_matrix* W, const void* x, int32_t x_dtype, int32_
  *   cand:   device int32 [n_rows][max_cand], weight-row indices; repeats allowed.
  *   n_cand: device int32 [n_rows], entries used per row.
  *   y:      device f32 [n_rows][max_cand].
- * W must be a GEMV-family matrix (any storage dtype).  Each y entry is
+ * W must be a GEMV or GEMV_MFMA family matrix.  Each y entry is
  * bit-identical to the same entry of gemv_rows(W, x) with an f32 output,
  * whatever the batch, list length or order (same K split, same summation
  * order), so the full head can serve as a cross-check of the gathered one.

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkd.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-FAMILY_GEMV, FAMILY_MFMA, FAMILY_MFMA_FP8 = 0, 1, 2
+FAMILY_GEMV, FAMILY_MFMA, FAMILY_MFMA_FP8, FAMILY_GEMV_MFMA = 0, 1, 2, 3
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory", 4: "out of bounds",
           5: "duplicate page", 6: "device error", 7: "invalid row"}
 

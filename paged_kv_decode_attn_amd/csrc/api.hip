@@ -114,7 +114,8 @@ pkd_status proj_validate(const ProjArgs& a, pkd_error* err) {
   const pkd_matrix* W = a.W;
   if (!W || !W->data) return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "matrix or its data is NULL");
   if (!valid_dtype(W->dtype)) return fail(err, PKD_ERR_INVALID_ARG, W->dtype, 0, "bad weight dtype %d", W->dtype);
-  if (W->family != PKD_FAMILY_GEMV && W->family != PKD_FAMILY_MFMA && W->family != PKD_FAMILY_MFMA_FP8)
+  if (W->family != PKD_FAMILY_GEMV && W->family != PKD_FAMILY_MFMA && W->family != PKD_FAMILY_MFMA_FP8 &&
+      W->family != PKD_FAMILY_GEMV_MFMA)
     return fail(err, PKD_ERR_INVALID_ARG, W->family, 0, "bad family %d", W->family);
   if (W->family == PKD_FAMILY_MFMA_FP8 && W->dtype != PKD_FP8_E4M3)
     return fail(err, PKD_ERR_UNSUPPORTED, W->dtype, PKD_FP8_E4M3, "the native fp8 family needs fp8 weights");
@@ -145,7 +146,12 @@ pkd_status proj_validate(const ProjArgs& a, pkd_error* err) {
     return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "row_scale must be 4-byte and rope_cs 8-byte aligned");
   if (!aligned16(a.x) || !aligned16(a.y) || !aligned16(a.residual) || !aligned16(a.y_bf16))
     return fail(err, PKD_ERR_INVALID_ARG, 0, 0, "device pointers must be 16-byte aligned");
-  if (W->family != PKD_FAMILY_GEMV) {
+  if (W->family == PKD_FAMILY_GEMV_MFMA) {
+    if (W->dtype == PKD_F32 || a.x_dtype != PKD_BF16)
+      return fail(err, PKD_ERR_UNSUPPORTED, a.x_dtype, PKD_BF16,
+                  "the GEMV_MFMA family needs bf16 or fp8 weights and bf16 activations");
+  }
+  if (tiled_family(W->family)) {
     const int kb = W->family == PKD_FAMILY_MFMA_FP8 ? 128 : 64;
     if (W->dtype == PKD_F32) return fail(err, PKD_ERR_UNSUPPORTED, 0, 0, "matrix-core family needs bf16 or fp8 weights");
     if (W->rows % 128 || W->cols % kb)
@@ -386,9 +392,9 @@ pkd_status gemv_gather_rows(const pkd_matrix* W, const void* x, int32_t x_dtype,
   a.out_dtype = PKD_F32;
   pkd_status s = proj_validate(a, err);
   if (s != PKD_OK) return s;
-  if (W->family != PKD_FAMILY_GEMV)
+  if (tiled_family(W->family))
     return fail(err, PKD_ERR_UNSUPPORTED, W->family, PKD_FAMILY_GEMV,
-                "gathered rows are evaluated with the vector family's summation order only");
+                "gathered rows are evaluated with the GEMV families' summation orders only");
   if (n_rows > 65535) return fail(err, PKD_ERR_UNSUPPORTED, n_rows, 65535, "at most 65535 activation rows");
   if (n_rows == 0) return PKD_OK;
   if (max_cand < 1) return fail(err, PKD_ERR_INVALID_ARG, max_cand, 1, "max_cand must be positive");
@@ -532,7 +538,7 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   // family quantises from the f32 / bf16 value itself)
   auto proj_in = [&](const pkd_matrix& W, const void* f32src, const void* bfsrc) -> std::pair<const void*, int> {
     if (!bf) return {f32src, PKD_F32};
-    if (W.family != PKD_FAMILY_GEMV && W.dtype == PKD_FP8_E4M3 && f32src) return {f32src, PKD_F32};
+    if (tiled_family(W.family) && W.dtype == PKD_FP8_E4M3 && f32src) return {f32src, PKD_F32};
     return {bfsrc, PKD_BF16};
   };
   ProjArgs p{};
@@ -568,7 +574,7 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   // 1. qkv = W_qkv x  (norm: W_qkv carries the gain, outputs times 1/rms(x);
   //    rope: the q and k heads rotated by the row's position)
   const bool norm = (L->flags & PKD_LAYER_NORM) != 0, rope = (L->flags & PKD_LAYER_ROPE) != 0;
-  const bool need_cast = bf && !(L->w_qkv.family != PKD_FAMILY_GEMV && L->w_qkv.dtype == PKD_FP8_E4M3);
+  const bool need_cast = bf && !(tiled_family(L->w_qkv.family) && L->w_qkv.dtype == PKD_FP8_E4M3);
   if (norm) {
     if ((s = rms_factor_launch(x, n, D, L->norm_eps, w.inv_x, need_cast ? w.x_in : nullptr, st, err))) return s;
   } else if (need_cast && (s = cast_bf16_launch(x, w.x_in, (int64_t)n * D, st, err))) {
@@ -616,7 +622,7 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   p.out_dtype = PKD_F32;
   p.residual = x;
   const bool need_h_bf16 =
-      F > 0 && bf && !(L->w_gate_up.family != PKD_FAMILY_GEMV && L->w_gate_up.dtype == PKD_FP8_E4M3);
+      F > 0 && bf && !(tiled_family(L->w_gate_up.family) && L->w_gate_up.dtype == PKD_FP8_E4M3);
   p.y_bf16 = need_h_bf16 ? w.h_in : nullptr;
   if ((s = proj_launch(p, w.proj_ws, w.proj_ws_bytes, st, err))) return s;
   if (F == 0) return ok(err);

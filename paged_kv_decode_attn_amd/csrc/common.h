@@ -116,6 +116,9 @@ struct AttnArgs {
 size_t attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t max_rows);
 pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err);
 
+// The tiled matrix-core families (large batches, K splits, workspace).
+inline bool tiled_family(int f) { return f == PKD_FAMILY_MFMA || f == PKD_FAMILY_MFMA_FP8; }
+
 // Projection launch used by gemv_rows and decode_step.
 struct ProjArgs {
   const pkd_matrix* W;

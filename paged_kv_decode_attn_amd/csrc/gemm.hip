@@ -566,7 +566,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* x, int K, ui
 static int splits_of(const pkd_matrix* W) { return W->k_splits > 1 ? W->k_splits : 1; }
 
 size_t proj_workspace_bytes(const pkd_matrix* W, int32_t max_rows) {
-  if (!W || max_rows <= 0 || W->family == PKD_FAMILY_GEMV) return 0;
+  if (!W || max_rows <= 0 || !tiled_family(W->family)) return 0;
   size_t b = 0;
   if (W->dtype == PKD_FP8_E4M3) b += align256((size_t)max_rows * W->cols) + align256(sizeof(float) * (size_t)max_rows);
   if (splits_of(W) > 1) b += align256(sizeof(float) * (size_t)splits_of(W) * max_rows * W->rows);
@@ -604,7 +604,7 @@ static int tile_m_for(int tiles_n, int splits, int M) {
 // (qkv 2, W_o 3, gate/up 1, down 3) and within 5% of it at batch 256 (qkv 4,
 // W_o 6, gate/up 1, down 8).
 int suggest_k_splits(int rows, int cols, int family, int typical_rows) {
-  if (family == PKD_FAMILY_GEMV || rows <= 0 || cols <= 0 || typical_rows <= 0) return 1;
+  if (!tiled_family(family) || rows <= 0 || cols <= 0 || typical_rows <= 0) return 1;
   constexpr double kFlopsPerCu = 4e12, kPartialBytesPerS = 5e12;
   const int tiles_n = (rows + TN - 1) / TN;
   int best = 1;
@@ -627,7 +627,7 @@ int suggest_k_splits(int rows, int cols, int family, int typical_rows) {
 pkd_status proj_launch(const ProjArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err) {
   const pkd_matrix& W = *a.W;
   if (a.n_rows == 0) return ok(err);
-  if (W.family == PKD_FAMILY_GEMV) return gemv_launch(a, stream, err);
+  if (!tiled_family(W.family)) return gemv_launch(a, stream, err);
   const size_t need = proj_workspace_bytes(a.W, a.n_rows);
   if (need && (!ws || ws_bytes < need))
     return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)need, (int64_t)(ws ? ws_bytes : 0),

@@ -294,6 +294,174 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
   }
 }
 
+// Matrix-core products for bf16 activations with bf16 or fp8 weights.  One
+// wave takes 16 weight rows (SILU: 8 gate rows and their 8 up rows) and 16
+// activation rows (rows past the batch are zeros), one 16 x 16 x 32 product per
+// 32 k.  The weights go straight from HBM into registers: lane (i, g) =
+// (l % 16, l / 16) holds 8 elements of weight row i at k = 32 t + 8 g, so one
+// wave load is 16 rows x 64 contiguous bytes (32 for fp8, widened exactly to
+// bf16 in registers); the activations are the other operand in the same
+// layout.  KS waves of a block (KS > 1: one row group per block) split the
+// k-steps into contiguous ranges and add their partial sums through LDS in
+// the order 0 .. KS - 1.  A product's column depends only on its own
+// activation row and the split only on the matrix shape, so a row's result
+// never depends on the batch.  This is the PKD_FAMILY_GEMV_MFMA family: the
+// matrix cores keep it near the weight stream up to 16 activation rows per
+// pass, where the vector-ALU form is bound by its multiply-adds from about 8,
+// but its 64-byte weight runs stream below the vector form's 1 KiB runs at
+// batch 1.
+// GATHER: one activation row per block column (column 0 of the product), the
+// 16 weight rows taken from its candidate list; everything else as dense.
+template <int WT, bool SILU, int KS, bool GATHER>
+__global__ __launch_bounds__(KS > 4 ? 64 * KS : 256) void gemv_mfma_kernel(GemvParams P) {
+  static_assert(!(GATHER && SILU), "gathered rows: no silu pair");
+  constexpr int NW = KS > 4 ? KS : 4;  // waves per block
+  constexpr int GPB = NW / KS;         // row groups per block
+  constexpr int NP = SILU ? 8 : 16;    // outputs per row group
+  const int wib = threadIdx.x >> 6, l = lane_id(), i = l & 15, g = l >> 4;
+  const int kw = wib % KS;
+  const int o0 = (blockIdx.x * GPB + wib / KS) * NP;
+  int n_out = P.n_out;
+  if constexpr (GATHER) n_out = min(max(P.n_cand[blockIdx.y], 0), P.max_cand);
+  if (o0 >= n_out) return;  // uniform over the block when KS > 1
+  // weight row of lane i (rows past the end repeat the last one; not stored)
+  int wr;
+  bool bad = false;
+  if constexpr (GATHER) {
+    const int j = P.cand[(int64_t)blockIdx.y * P.max_cand + min(o0 + i, n_out - 1)];
+    bad = j < 0 || j >= P.rows;
+    wr = bad ? 0 : j;
+  } else if constexpr (SILU) {
+    wr = i < 8 ? min(o0 + i, P.n_out - 1) : P.n_out + min(o0 + i - 8, P.n_out - 1);
+  } else {
+    wr = min(o0 + i, P.rows - 1);
+  }
+  // activation row of lane i (the product's column i)
+  const int xr = GATHER ? (i == 0 ? (int)blockIdx.y : -1) : (blockIdx.y * 16 + i < P.n_rows ? blockIdx.y * 16 + i : -1);
+  constexpr int WB = WT == 1 ? 16 : 8;  // weight bytes per lane and k-step
+  const uint8_t* wp = P.W + (int64_t)wr * P.cols * (WT == 1 ? 2 : 1) + WB * g;
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(P.x) + (int64_t)(xr < 0 ? 0 : xr) * P.x_stride + 8 * g;
+  const int nst = P.cols / 32;
+  const int t0 = nst * kw / KS, t1 = nst * (kw + 1) / KS;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 8;
+  for (int t = t0; t < t1; t += U) {
+    u32x4 wv[U], xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t + u >= t1) break;
+      if constexpr (WT == 1) {
+        wv[u] = *reinterpret_cast<const u32x4*>(wp + 64 * (int64_t)(t + u));
+      } else {
+        const u32x2 c = *reinterpret_cast<const u32x2*>(wp + 32 * (int64_t)(t + u));
+        wv[u] = u32x4{c.x, c.y, 0u, 0u};
+      }
+      xv[u] = xr >= 0 ? *reinterpret_cast<const u32x4*>(xp + 32 * (int64_t)(t + u)) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t + u >= t1) break;
+      u32x4 a = wv[u];
+      if constexpr (WT == 2) {
+        const u32x2 lo = fp8x4_to_bf16x4(wv[u].x), hi = fp8x4_to_bf16x4(wv[u].y);
+        a = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, xv[u]),
+                                                    acc, 0, 0, 0);
+    }
+  }
+  if constexpr (KS > 1) {
+    __shared__ f32x4_t part[KS][64];
+    part[kw][l] = acc;
+    __syncthreads();
+    if (kw != 0) return;
+    f32x4_t tsum = part[0][l];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) tsum += part[w][l];
+    acc = tsum;
+  }
+  // lane (rg, col) holds outputs o0 + 4 rg + v (v < 4) of activation column col
+  const int col = l & 15, rg = l >> 4;
+  if constexpr (GATHER) {
+    bool bv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) bv[v] = __shfl((int)bad, 4 * rg + v, kWave) != 0;
+    if (col != 0) return;
+    float* y = reinterpret_cast<float*>(P.y) + (int64_t)blockIdx.y * P.max_cand;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int o = o0 + 4 * rg + v;
+      if (o < n_out) y[o] = bv[v] ? __builtin_nanf("") : acc[v] * P.w_scale;
+    }
+    return;
+  }
+  float vo[4];
+  int ob;  // first output of this lane
+  if constexpr (SILU) {
+    float up[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) up[v] = shfl_xor(acc[v], 32);
+    if (rg >= 2) return;
+    const int r = blockIdx.y * 16 + col;
+    if (r >= P.n_rows) return;
+    const float rsc = P.row_scale ? P.row_scale[r] : 1.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float gt = acc[v] * P.w_scale, u = up[v] * P.w_scale;
+      if (P.row_scale) { gt *= rsc; u *= rsc; }
+      vo[v] = silu(gt) * u;
+    }
+    ob = o0 + 4 * rg;
+  } else {
+    const int r = blockIdx.y * 16 + col;
+    if (r >= P.n_rows) return;
+    const float rsc = P.row_scale ? P.row_scale[r] : 1.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      vo[v] = acc[v] * P.w_scale;
+      if (P.row_scale) vo[v] *= rsc;
+    }
+    ob = o0 + 4 * rg;
+    if (P.rope_cs && ob < P.rope_cols) {
+      rope_pair(P.rope_cs, P.rope_hd, r, ob, vo[0], vo[1]);
+      rope_pair(P.rope_cs, P.rope_hd, r, ob + 2, vo[2], vo[3]);
+    }
+  }
+  const int r = blockIdx.y * 16 + col;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int o = ob + v;
+    if (o >= P.n_out) break;
+    float val = vo[v];
+    if constexpr (!SILU) {
+      if (P.residual) val += P.residual[(int64_t)r * P.n_out + o];
+    }
+    if (P.y_bf16) reinterpret_cast<uint16_t*>(P.y)[(int64_t)r * P.y_stride + o] = (uint16_t)f32_to_bf16_bits(val);
+    else reinterpret_cast<float*>(P.y)[(int64_t)r * P.y_stride + o] = val;
+    if (P.y2) P.y2[(int64_t)r * P.n_out + o] = (uint16_t)f32_to_bf16_bits(val);
+  }
+}
+
+// K split of the matrix-core form: a function of the weight-row count only
+// (16-row groups), so a matrix and any gathered subset of its rows split alike.
+static int gemv_mfma_k_split(int rows) {
+  const int groups = (rows + 15) / 16;
+  return groups < 1024 ? 8 : groups < 4096 ? 4 : 1;
+}
+
+template <int WT, bool SILU, bool GATHER>
+static void launch_mfma(const GemvParams& P, int tiles_y, hipStream_t st) {
+  constexpr int NP = SILU ? 8 : 16;
+  const int groups = ((GATHER ? P.max_cand : P.n_out) + NP - 1) / NP;
+  const int ks = gemv_mfma_k_split(P.rows);
+  if (ks == 8)
+    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 8, GATHER>), dim3(groups, tiles_y), dim3(512), 0, st, P);
+  else if (ks == 4)
+    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 4, GATHER>), dim3(groups, tiles_y), dim3(256), 0, st, P);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 1, GATHER>), dim3((groups + 3) / 4, tiles_y), dim3(256), 0, st, P);
+}
+
 // K split of a matrix: 4 when its row groups alone would give fewer than
 // 8192 waves (a function of the shape, never of the batch).
 static int gemv_k_split(int n_out, int np) { return (n_out + np - 1) / np < 8192 ? 4 : 1; }
@@ -367,7 +535,9 @@ pkd_status gemv_gather_launch(const pkd_matrix& W, const void* x, int32_t x_dtyp
   P.cand = cand;
   P.n_cand = n_cand;
   P.max_cand = max_cand;
-  if (W.dtype == PKD_F32) launch_gather_w<0>(P, x_dtype, stream);
+  if (W.family == PKD_FAMILY_GEMV_MFMA && W.dtype == PKD_BF16) launch_mfma<1, false, true>(P, n_rows, stream);
+  else if (W.family == PKD_FAMILY_GEMV_MFMA) launch_mfma<2, false, true>(P, n_rows, stream);
+  else if (W.dtype == PKD_F32) launch_gather_w<0>(P, x_dtype, stream);
   else if (W.dtype == PKD_BF16) launch_gather_w<1>(P, x_dtype, stream);
   else launch_gather_w<2>(P, x_dtype, stream);
   return check_launch(err, "gemv_gather_rows");
@@ -394,9 +564,18 @@ pkd_status gemv_launch(const ProjArgs& a, hipStream_t stream, pkd_error* err) {
   P.rope_cols = a.rope_cols;
   P.rope_hd = a.rope_hd;
   const bool silu = a.silu_pair != 0;
-  if (W.dtype == PKD_F32) launch_w<0>(P, a.x_dtype, silu, stream);
-  else if (W.dtype == PKD_BF16) launch_w<1>(P, a.x_dtype, silu, stream);
-  else launch_w<2>(P, a.x_dtype, silu, stream);
+  const int ty = (a.n_rows + 15) / 16;
+  if (W.family == PKD_FAMILY_GEMV_MFMA && W.dtype == PKD_BF16) {
+    if (silu) launch_mfma<1, true, false>(P, ty, stream); else launch_mfma<1, false, false>(P, ty, stream);
+  } else if (W.family == PKD_FAMILY_GEMV_MFMA) {
+    if (silu) launch_mfma<2, true, false>(P, ty, stream); else launch_mfma<2, false, false>(P, ty, stream);
+  } else if (W.dtype == PKD_F32) {
+    launch_w<0>(P, a.x_dtype, silu, stream);
+  } else if (W.dtype == PKD_BF16) {
+    launch_w<1>(P, a.x_dtype, silu, stream);
+  } else {
+    launch_w<2>(P, a.x_dtype, silu, stream);
+  }
   return check_launch(err, "gemv_rows");
 }
 

@@ -194,3 +194,20 @@ def test_norm_rope_refusals_are_typed(pkd):
         st = L.gemv_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 1, 1 << 21, ctypes.byref(ep), None, 0, None,
                          ctypes.byref(err))
         assert st == 1, (rope_cols, hd, silu)
+
+
+def test_gemv_mfma_family_refusals(pkd):
+    """The matrix-core GEMV family takes bf16 or fp8 weights and bf16 activations only."""
+    err = pkd.pkd_error()
+    ep = pkd.pkd_epilogue(pkd.F32, None, 0, None)
+    W = pkd.pkd_matrix(1 << 20, 100, 256, pkd.BF16, 1.0, pkd.FAMILY_GEMV_MFMA)
+    assert pkd.lib().gemv_rows(ctypes.byref(W), 1 << 20, pkd.F32, 4, 1 << 21, ctypes.byref(ep), None, 0, None,
+                               ctypes.byref(err)) == 2
+    W = pkd.pkd_matrix(1 << 20, 100, 256, pkd.F32, 1.0, pkd.FAMILY_GEMV_MFMA)
+    assert pkd.lib().gemv_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 4, 1 << 21, ctypes.byref(ep), None, 0, None,
+                               ctypes.byref(err)) == 2
+    W = pkd.pkd_matrix(1 << 20, 100, 256, pkd.BF16, 1.0, 4)
+    assert pkd.lib().gemv_rows(ctypes.byref(W), 1 << 20, pkd.BF16, 4, 1 << 21, ctypes.byref(ep), None, 0, None,
+                               ctypes.byref(err)) == 1  # no such family
+    assert pkd.pkd_gemv_workspace_bytes(pkd.pkd_matrix(1 << 20, 128, 256, pkd.FP8_E4M3, 0.01,
+                                                       pkd.FAMILY_GEMV_MFMA), 64) == 0

@@ -89,17 +89,25 @@ GEMV_CASES = [
 ]
 
 
-@pytest.mark.parametrize("wdt,xdt,rows,cols,n,silu,res,out", GEMV_CASES)
-def test_gemv_parity(H, orc, wdt, xdt, rows, cols, n, silu, res, out):
+GEMV_FAMILY_CASES = [(0,) + c for c in GEMV_CASES] + [
+    (3,) + c for c in GEMV_CASES if c[1] == wl.BF16 and c[0] != wl.F32] + [
+    (3, wl.BF16, wl.BF16, 1000, 3584, 37, False, True, wl.F32),  # three 16-row activation tiles, ragged
+    (3, wl.FP8, wl.BF16, 2 * 520, 1024, 20, True, False, wl.BF16),
+]
+
+
+@pytest.mark.parametrize("fam,wdt,xdt,rows,cols,n,silu,res,out", GEMV_FAMILY_CASES)
+def test_gemv_parity(H, orc, fam, wdt, xdt, rows, cols, n, silu, res, out):
+    """Vector family (0) and the matrix-core GEMV family (3) against the oracle."""
     seed = rows + cols + n
     W, s = make_w(rows, cols, wdt, seed)
     x = make_x(n, cols, xdt, seed)
     residual = torch.randn((n, rows)) if res else None
-    y, yb = run_proj(H, W, rows, cols, wdt, s, 0, x, xdt, n, out, silu, residual, y2=True)
+    y, yb = run_proj(H, W, rows, cols, wdt, s, fam, x, xdt, n, out, silu, residual, y2=True)
     want = oracle_proj(orc, W, wdt, s, x, xdt, 0, silu, residual)
     got = H.values(y, out)
     e = H.rel_err(got, want)
-    print(f"gemv w{wdt} x{xdt} {rows}x{cols} n={n} silu={silu}: {e:.2e}")
+    print(f"gemv family {fam} w{wdt} x{xdt} {rows}x{cols} n={n} silu={silu}: {e:.2e}")
     assert e <= (TOL if out == wl.F32 else TOL_BF16)
     assert H.rel_err(H.values(yb, wl.BF16), want) <= TOL_BF16
 
@@ -166,7 +174,7 @@ def test_mfma_tile_height_invariance(H):
         assert torch.equal(part.cpu(), full[r:r + n]), (r, n)
 
 
-@pytest.mark.parametrize("family,rows", [(0, 256), (0, 33000), (1, 256)])
+@pytest.mark.parametrize("family,rows", [(0, 256), (0, 33000), (1, 256), (3, 256), (3, 70000)])
 def test_projection_batch_invariance(H, family, rows):
     """A row's outputs are bit-identical alone, in any batch size (the vector
     family's register tile changes with the batch) and at any position; for
@@ -219,10 +227,10 @@ def gather_lists(n, rows, max_cand, seed):
     return cand, n_cand
 
 
-def run_gather(W, rows, cols, wdt, s, x, xdt, n, cand, n_cand, fill=12345.0):
+def run_gather(W, rows, cols, wdt, s, x, xdt, n, cand, n_cand, fill=12345.0, fam=0):
     import paged_kv_decode_attn_amd as pkd
     Wd = W.cuda()  # the matrix descriptor holds a raw pointer: keep the tensor alive
-    M = pkd.make_matrix(Wd, rows, cols, wdt, s, 0)
+    M = pkd.make_matrix(Wd, rows, cols, wdt, s, fam)
     y = torch.full((n, cand.shape[1]), fill, dtype=torch.float32, device="cuda")
     pkd.gemv_gather_rows(M, x.cuda(), xdt, n, torch.from_numpy(cand).cuda(), torch.from_numpy(n_cand).cuda(),
                          cand.shape[1], y)
@@ -249,8 +257,12 @@ def check_gathered(got, want, dense, cand, n_cand, fill):
     return e
 
 
-@pytest.mark.parametrize("wdt,xdt,rows,cols,n,max_cand", GATHER_CASES)
-def test_gather_parity(H, orc, wdt, xdt, rows, cols, n, max_cand):
+GATHER_FAMILY_CASES = [(0,) + c for c in GATHER_CASES] + [
+    (3,) + c for c in GATHER_CASES if c[1] == wl.BF16 and c[0] != wl.F32]
+
+
+@pytest.mark.parametrize("fam,wdt,xdt,rows,cols,n,max_cand", GATHER_FAMILY_CASES)
+def test_gather_parity(H, orc, fam, wdt, xdt, rows, cols, n, max_cand):
     """Logits of the listed rows: oracle parity, and bit-identical to the same
     entries of the dense head (gemv_rows over the whole matrix)."""
     seed = rows + cols + n
@@ -258,16 +270,17 @@ def test_gather_parity(H, orc, wdt, xdt, rows, cols, n, max_cand):
     x = make_x(n, cols, xdt, seed)
     cand, n_cand = gather_lists(n, rows, max_cand, seed)
     fill = 12345.0
-    got = run_gather(W, rows, cols, wdt, s, x, xdt, n, cand, n_cand, fill)
+    got = run_gather(W, rows, cols, wdt, s, x, xdt, n, cand, n_cand, fill, fam)
     xv = (orc.bf16_value(wl.to_numpy_codes(x, wl.BF16)) if xdt == wl.BF16 else x.numpy().astype(np.float64))
     want = orc.matvec_gathered(wdt, wl.to_numpy_codes(W, wdt), s, xv, cand, n_cand, fill)
-    dense, _ = run_proj(H, W, rows, cols, wdt, s, 0, x, xdt, n, wl.F32)
+    dense, _ = run_proj(H, W, rows, cols, wdt, s, fam, x, xdt, n, wl.F32)
     e = check_gathered(got, want, dense.cpu().numpy(), cand, n_cand, fill)
-    print(f"gather w{wdt} x{xdt} {rows}x{cols} n={n} max_cand={max_cand}: {e:.2e}")
+    print(f"gather family {fam} w{wdt} x{xdt} {rows}x{cols} n={n} max_cand={max_cand}: {e:.2e}")
     assert e <= TOL
 
 
-def test_gather_full_vocabulary_head(H, orc):
+@pytest.mark.parametrize("fam", [0, 3])
+def test_gather_full_vocabulary_head(H, orc, fam):
     """The tied-embedding head at its full size (151,936 x 2,048 bf16), 64
     rows of up to 28 candidates: every entry bit-identical to the dense head,
     and the oracle on a sample of rows."""
@@ -278,7 +291,7 @@ def test_gather_full_vocabulary_head(H, orc):
     Wd = (torch.randn((V, D), generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
     x = (torch.randn((n, D), generator=g, device="cuda")).to(torch.bfloat16).view(torch.int16)
     cand, n_cand = wl.head_candidates(n, V, C, 78)
-    M = pkd.make_matrix(Wd, V, D, wl.BF16, 1.0, 0)
+    M = pkd.make_matrix(Wd, V, D, wl.BF16, 1.0, fam)
     y = torch.full((n, C), -5.0, device="cuda")
     pkd.gemv_gather_rows(M, x, wl.BF16, n, torch.from_numpy(cand).cuda(), torch.from_numpy(n_cand).cuda(), C, y)
     dense = torch.empty((n, V), device="cuda")
@@ -353,6 +366,8 @@ EPI_CASES = [
     (1, wl.FP8, wl.BF16, 768, 1024, 33, 1, False),
     (1, wl.BF16, wl.BF16, 2 * 256, 1024, 90, 3, True),
     (2, wl.FP8, wl.F32, 768, 1024, 40, 1, False),
+    (3, wl.BF16, wl.BF16, 768, 1024, 21, 1, False),
+    (3, wl.FP8, wl.BF16, 2 * 256, 1024, 9, 1, True),
 ]
 
 
