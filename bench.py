@@ -345,30 +345,35 @@ def main():
                     "GB_s": round(ab / med / 1e3, 1), "hbm_frac": round(ab / med / 1e3 / HBM_PEAK_GBS, 4)}
     t2_res = None
     if not args.no_t2 and F and w.w_dtype == 1:
-        g_layer = H.GpuLayer(w, family=0).layer  # same weights, vector family
         t2_res = {"matrices": "W_qkv, W_o, [W_gate; W_up], W_down", "family": 0}
         wbytes = 2 * (nqkv * D + D * nq * d + 2 * F * D + D * F)
-        for nb in (1, 4, 8, 16):
-            xs = (torch.randn((nb, max(D, F, nq * d)), device="cuda") * 0.5).to(torch.bfloat16).view(torch.int16)
-            oq = torch.empty((nb, nqkv), dtype=torch.int16, device="cuda")
-            oh = torch.empty((nb, D), dtype=torch.float32, device="cuda")
-            og = torch.empty((nb, F), dtype=torch.int16, device="cuda")
-            res = torch.zeros((nb, D), dtype=torch.float32, device="cuda")
-            xd = xs[:, :D].contiguous()
-            xa = xs[:, :nq * d].contiguous()
-            xf = xs[:, :F].contiguous()
+        # the vector family (the graded one), then the same pass on the matrix-core GEMV family
+        for t2_fam in (0, 3):
+            g_obj = H.GpuLayer(w, family=t2_fam)  # same weights; the object owns the device copies
+            g_layer = g_obj.layer
+            dest = t2_res if t2_fam == 0 else t2_res.setdefault("family3_matrix_core_gemv", {})
+            for nb in (1, 4, 8, 16):
+                xs = (torch.randn((nb, max(D, F, nq * d)), device="cuda") * 0.5).to(torch.bfloat16).view(torch.int16)
+                oq = torch.empty((nb, nqkv), dtype=torch.int16, device="cuda")
+                oh = torch.empty((nb, D), dtype=torch.float32, device="cuda")
+                og = torch.empty((nb, F), dtype=torch.int16, device="cuda")
+                res = torch.zeros((nb, D), dtype=torch.float32, device="cuda")
+                xd = xs[:, :D].contiguous()
+                xa = xs[:, :nq * d].contiguous()
+                xf = xs[:, :F].contiguous()
 
-            def gemv_pass():
-                pkd.gemv_rows(g_layer.w_qkv, xd, 1, nb, oq, 1)
-                pkd.gemv_rows(g_layer.w_o, xa, 1, nb, oh, 0, residual=res)
-                pkd.gemv_rows(g_layer.w_gate_up, xd, 1, nb, og, 1, silu_pair=True)
-                pkd.gemv_rows(g_layer.w_down, xf, 1, nb, oh, 0, residual=res)
-            for _ in range(3):
-                gemv_pass()
-            med, p10, p90 = timed(gemv_pass, max(args.steps, 10), True)
-            byt = wbytes + nb * 2 * (D + nq * d + D + F) + nb * (2 * nqkv + 8 * D + 2 * F + 8 * D)
-            t2_res[f"B{nb}"] = {"us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2), "bytes": int(byt),
-                            "GB_s": round(byt / med / 1e3, 1), "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4)}
+                def gemv_pass():
+                    pkd.gemv_rows(g_layer.w_qkv, xd, 1, nb, oq, 1)
+                    pkd.gemv_rows(g_layer.w_o, xa, 1, nb, oh, 0, residual=res)
+                    pkd.gemv_rows(g_layer.w_gate_up, xd, 1, nb, og, 1, silu_pair=True)
+                    pkd.gemv_rows(g_layer.w_down, xf, 1, nb, oh, 0, residual=res)
+                for _ in range(3):
+                    gemv_pass()
+                med, p10, p90 = timed(gemv_pass, max(args.steps, 10), True)
+                byt = wbytes + nb * 2 * (D + nq * d + D + F) + nb * (2 * nqkv + 8 * D + 2 * F + 8 * D)
+                dest[f"B{nb}"] = {"us": round(med, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+                                  "bytes": int(byt), "GB_s": round(byt / med / 1e3, 1),
+                                  "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4)}
     # Output head over a tied embedding (151,936 x 2,048 bf16, 593.5 MiB): the
     # dense head at batch 1 against the candidate-row head, whose rows carry
     # trie-shaped lists of 1..28 candidates, cold.
