@@ -69,7 +69,9 @@ typedef enum {
 } pkd_dtype;
 
 typedef enum {
-  PKD_FAMILY_GEMV = 0,    /* one 64-lane wavefront per weight row, vector ALU, fp32 accumulate */
+  PKD_FAMILY_GEMV = 0,    /* decode batches: one 64-lane wavefront per 4 weight rows, each lane
+                             reading 16-byte vectors (1 KiB runs per wave load), vector ALU,
+                             fp32 accumulate */
   PKD_FAMILY_MFMA = 1,    /* tiled matrix-core contraction for large batches: bf16 operands, or
                              fp8 operands decoded exactly to bf16 on chip; products exact and
                              sums with fp32 accumulation */

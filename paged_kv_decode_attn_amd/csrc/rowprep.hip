@@ -22,12 +22,14 @@
 
 namespace pkd {
 
-__global__ __launch_bounds__(256) void rms_factor_kernel(const float* x, int n, int cols, float eps, float* inv,
-                                                         uint16_t* xb) {
+__global__ __launch_bounds__(256) void rms_factor_kernel(const float* __restrict__ x, int n, int cols, float eps,
+                                                         float* __restrict__ inv, uint16_t* __restrict__ xb) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6), l = lane_id();
   if (r >= n) return;
   const float* row = x + (int64_t)r * cols;
   float ss = 0.f;
+  // unrolled so that several 1 KiB wave loads of the row are in flight at once
+#pragma unroll 4
   for (int j = l; j < cols / 4; j += 64) {
     const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + 4 * j);
     ss = fmaf(v[0], v[0], ss);
