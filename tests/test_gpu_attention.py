@@ -359,3 +359,23 @@ def test_prefill_tile_invalid_rows(H, chunk):
     assert (out[122:].view(torch.int16) == 0).all()
     ref = H.run_attention(pool, seq[:122], pos[:122], q[:122].contiguous(), None, None, distinct=True).cpu()
     assert torch.equal(out[:122].view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("kvt,chunk", [(wl.BF16, 2), (wl.BF16, 100), (wl.FP8, 3), (wl.F32, 100)])
+def test_full_tables(H, orc, kvt, chunk):
+    """Rows whose token lands in the last slot of the last page their table
+    holds (no spare pages): the largest position a table admits, with and
+    without the append fused."""
+    lens = (32, 64, 96, 320)
+    w = wl.make("attn", "cpu", seed=21 + kvt + chunk, n_q=8, n_kv=2, d=128, kv_dtype=kvt, lens=lens, append=True,
+                chunk=chunk, extra_pages=0)
+    assert all(int(w.pos[s]) == 32 * int(w.counts[s]) - 1 for s in range(len(lens)))
+    want = oracle_attn(orc, w, w.seq, w.pos, w.q, w.k_new, w.v_new)
+    for distinct in (False, True):
+        pool = H.GpuPool(w)
+        out = H.run_attention(pool, w.seq, w.pos, w.q.cuda(), w.k_new.cuda(), w.v_new.cuda(), wl.F32, distinct)
+        import paged_kv_decode_attn_amd as pkd
+        pkd.pkd_pool_check(pool.handle)
+        e = H.rel_err(out.cpu().numpy(), want)
+        print(f"full tables kv{kvt} chunk {chunk} distinct={distinct}: {e:.2e}")
+        assert e <= TOL_F32_OUT
