@@ -261,7 +261,7 @@ def _b1_06(gen, rng, dev, L: int = 2048, chunk: int = 2, family: int = GEMV):
                     np.zeros(1, np.int32), np.asarray([L - 1], np.int32), x, ws, sc)
 
 
-def _mixed_06(gen, rng, dev, n_decode: int = 512, chunk_rows: int = 256, chunk: int = 4,
+def _mixed_06(gen, rng, dev, n_decode: int = 512, chunk_rows: int = 256, chunk: int = 8,
               family: int = MFMA, long_max: int = 2662):
     """0.6B-class layer, mixed step: n_decode decode rows (80% with context
     U{100..200}, 20% U{1000..long_max}) plus `chunk_rows` rows of one 2,662-token
