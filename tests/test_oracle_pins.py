@@ -647,3 +647,94 @@ def test_step_rows_independent_and_sequential(orc, norm_rope):
         hj = orc.History([np.concatenate([s2k, kk[:j]])], [np.concatenate([s2v, vv[:j]])], 1, nkv, d)
         r = orc.decode_step(layer, hj, [0], [base + j], xs[j:j + 1])
         assert np.array_equal(r["y"][0], one["y"][j])
+
+
+# ----------------------------------------------------------------------------- brute force in long double
+def _brute_step(layer, hist, seq, pos, x):
+    """The whole step written out with numpy long-double loops, f32 tier: the
+    stored weights, qkv rounded to f32 (after the norm factor and rotary
+    positions when on), every row appended before any row attends, softmax
+    with the maximum subtracted, attn and a rounded to f32, f32 residual
+    inputs.  Independent of the C oracle's code."""
+    LD = np.longdouble
+    D, nq, nkv, d, F = (layer[k] for k in ("hidden", "n_q", "n_kv", "head_dim", "ffn"))
+    f32 = lambda v: np.asarray(v, np.float32).astype(LD)
+    Wq, Wo, Wg, Wd = (layer[k].astype(LD) for k in ("w_qkv", "w_o", "w_gu", "w_d"))
+    n = len(seq)
+    X = x.astype(LD)
+
+    def inv_rms(z):
+        return LD(1) / np.sqrt(np.sum(z * z) / LD(len(z)) + LD(layer.get("norm_eps", 1e-6)))
+
+    def rope(v, p):
+        out = v.copy()
+        base = LD(layer.get("rope_base", 10000.0))
+        for i in range(d // 2):
+            th = LD(p) * base ** (LD(-2 * i) / LD(d))
+            c, s = np.cos(th), np.sin(th)
+            for h in range(nq + nkv):
+                a, b = v[h * d + 2 * i], v[h * d + 2 * i + 1]
+                out[h * d + 2 * i], out[h * d + 2 * i + 1] = a * c - b * s, a * s + b * c
+        return out
+    qkv = []
+    for r in range(n):
+        v = Wq @ f32(x[r])
+        if layer.get("norm"):
+            v = v * inv_rms(X[r])
+        if layer.get("rope"):
+            v = rope(v, pos[r])
+        qkv.append(f32(v))
+    qkv = np.stack(qkv)
+    K = {s: [hist.k[hist.hist_off[s] + t].astype(LD) for t in range(hist.hist_len[s])] for s in set(seq)}
+    V = {s: [hist.v[hist.hist_off[s] + t].astype(LD) for t in range(hist.hist_len[s])] for s in set(seq)}
+    for r in range(n):
+        s, p = seq[r], pos[r]
+        kr = qkv[r, nq * d:(nq + nkv) * d].reshape(nkv, d)
+        vr = qkv[r, (nq + nkv) * d:].reshape(nkv, d)
+        while len(K[s]) <= p:
+            K[s].append(None)
+            V[s].append(None)
+        K[s][p], V[s][p] = kr, vr
+    G = nq // nkv
+    attn = np.zeros((n, nq * d), LD)
+    for r in range(n):
+        s, p = seq[r], pos[r]
+        for h in range(nq):
+            g = h // G
+            q = qkv[r, h * d:(h + 1) * d]
+            sc = np.array([np.sum(q * K[s][t][g]) / np.sqrt(LD(d)) for t in range(p + 1)], LD)
+            w = np.exp(sc - sc.max())
+            w = w / w.sum()
+            attn[r, h * d:(h + 1) * d] = sum(w[t] * V[s][t][g] for t in range(p + 1))
+    attn = f32(attn)
+    h = X + attn @ Wo.T
+    hin = f32(h)
+    gu = hin @ Wg.T
+    if layer.get("norm"):
+        fac = np.array([inv_rms(h[r]) for r in range(n)], LD)
+        gu = gu * fac[:, None]
+    a = f32(gu[:, :F] / (LD(1) + np.exp(-gu[:, :F])) * gu[:, F:])
+    y = h + a @ Wd.T
+    return dict(qkv=qkv, attn=attn, h=h, a=a, y=y)
+
+
+@pytest.mark.parametrize("norm_rope", [False, True])
+def test_step_vs_long_double_brute_force(orc, norm_rope):
+    """The C oracle's whole step against a numpy long-double brute force on a
+    tiny f32 layer (several rows of one sequence, GQA): the f32-rounded
+    intermediates equal, h and y within 1e-12 relative."""
+    rng = np.random.default_rng(40)
+    layer, hist, seq, pos, x = _small_layer(orc, rng, w_dtype=0, kv_dtype=0, D=64, nq=4, nkv=2, d=16, F=64,
+                                            lens=(1, 5, 33))
+    if norm_rope:
+        layer.update(norm=True, rope=True, norm_eps=1e-6, rope_base=10000.0)
+    seq = np.asarray([0, 1, 2, 2], np.int32)
+    pos = np.asarray([0, 4, 32, 33], np.int32)
+    x = np.concatenate([x, x[2:3] * 0.5], 0).astype(np.float32) * 2.0
+    out = orc.decode_step(layer, hist, seq, pos, x)
+    want = _brute_step(layer, hist, seq, pos, x)
+    for k in ("qkv", "attn", "a"):
+        assert np.array_equal(out[k], want[k].astype(np.float64)), k
+    for k in ("h", "y"):
+        ref = want[k].astype(np.float64)
+        assert np.allclose(out[k], ref, rtol=1e-12, atol=1e-13), k
