@@ -294,6 +294,7 @@ def test_stage_parity(H, orc, name, kw, bar):
     ("0.6b-mixed-bf16", dict(n_decode=24, chunk_rows=12, chunk=4, long_max=1400), 8, False),
     ("7b-b4096-fp8", dict(n=64, L=100), 64, False),
     ("0.6b-mixed-bf16", dict(n_decode=24, chunk_rows=12, chunk=4, long_max=1400), 8, True),
+    ("prefill-chunk", dict(layer="0.6b", p0=1024, n=256), 256, False),  # shared tiles inside the graph
 ])
 def test_step_graph_replay(H, name, kw, hint, norm_rope):
     """decode_step captured in a graph and replayed several times, with eager
