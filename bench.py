@@ -313,12 +313,12 @@ def main():
                 "algorithmic_bytes": int(sbytes_m[dom])}
     value = total_bytes / (ms_step * 1e-3) / 1e9
 
-    # ---------------------------------------------------------------- T1 / T2
-    # T1: append + paged attention alone on this workload's pool and rows, cold
+    # ---------------------------------------------------------------- attention and GEMV alone
+    # t1_attention: append + paged attention alone on this workload's pool and rows, cold
     # (a 2 GiB buffer is read before every rep, outside the events, so no page
     # is left in L2 or the 256 MB MALL; read, not written, so that no dirty
     # lines are left to be written back during the timed call) and warm.
-    # T2: the vector-family GEMV over every weight matrix of the layer at
+    # t2_gemv: the vector-family GEMV over every weight matrix of the layer at
     # decode batches 1..16, cold.
     flush = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
     flush_sum = torch.empty((), dtype=torch.float32, device="cuda")
