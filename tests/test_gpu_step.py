@@ -382,3 +382,17 @@ def test_prefill_chunk_step(H, orc, layer):
     for r in (0, 100, 255):
         one = lay.step(pool, w.seq[r:r + 1], w.pos[r:r + 1], w.x[r:r + 1]).cpu()
         assert torch.equal(one[0], y[r]), r
+
+
+def test_step_matrix_core_gemv_family(H, orc):
+    """The whole step with every projection on the matrix-core GEMV family:
+    oracle parity, and a row alone gives the bits it gives in the batch."""
+    w = wl.make("0.6b-mixed-bf16", "cpu", n_decode=24, chunk_rows=12, chunk=4, long_max=1400, family=3)
+    layer = H.GpuLayer(w)
+    full = layer.step(H.GpuPool(w), w.seq, w.pos, w.x).cpu()
+    want = oracle_rows(orc, w, np.arange(w.n_rows))
+    check(H, full.numpy(), want["y"], BAR_BF16, "0.6b-mixed small, GEMV_MFMA family y")
+    for r in (0, 13, 30):
+        one = layer.step(H.GpuPool(w), w.seq[r:r + 1], w.pos[r:r + 1], w.x[r:r + 1]).cpu()
+        if w.seq[r] != w.seq.max():  # decode rows alone (slice rows need the earlier slice tokens)
+            assert torch.equal(one[0], full[r]), r
