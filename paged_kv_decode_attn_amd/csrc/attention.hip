@@ -494,6 +494,10 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
   // the page is read exactly as a separate append pass would leave it.  No
   // other wave of the launch reads that page.
   const int own = FUSE ? p_row / kPage : -1;
+  // the own page's table entry is read directly: the lane window above only
+  // moves forward one page at a time, and the own page may lie 64 or more
+  // pages past pg0
+  const int own_page = FUSE ? trow[own] : 0;
   NewToken<KVT, D> nt;
   if constexpr (FUSE) append_load<KVT, D>(P, r, g, nt);
   u32x4 kr[GE::NL], vr[GE::NL];
@@ -503,12 +507,12 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
     else load_block<KVT, D>(base + (uint64_t)page_of(pg) * P.page_stride + c * P.block_bytes, regs);
   };
   if (FUSE && own == pg0) {
-    append_store<KVT, D>(P, g, page_of(own), p_row % kPage, nt);
+    append_store<KVT, D>(P, g, own_page, p_row % kPage, nt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   load(pg0, 0, kr);
   load(pg0, 1, vr);
-  if (FUSE && own != pg0) append_store<KVT, D>(P, g, page_of(own), p_row % kPage, nt);
+  if (FUSE && own != pg0) append_store<KVT, D>(P, g, own_page, p_row % kPage, nt);
   for (int pg = pg0; pg < pg1; ++pg) {
     const bool nxt = pg + 1 < pg1;
     f32x4_t S[2];
@@ -675,7 +679,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 // finished here; the others leave (m, l, O) at record (row, chunk) for the
 // ordered merge.  A refused row is reported here (chunk 0, kv head 0) and
 // zeroed by the merge.
-template <int KVT, int D>
+//   FUSE: every sequence has one row in the launch; the wave of the row's last
+//   chunk (the one holding its own page) also appends the row's token, as in
+//   the direct kernel, and no other chunk reads that page.
+template <int KVT, int D, bool FUSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunked_kernel(AttnParams P) {
   using GE = Geo<KVT, D>;
   const int cw = (P.max_ch + 3) / 4;
@@ -692,7 +699,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
   const int tab = pg0 + l < pg1 ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
   Acc<KVT, D> A;
-  run_unit<KVT, D>(P, A, r, s, p, g, pg0, pg1, tab);
+  if (FUSE && c == nch - 1) run_unit<KVT, D, true>(P, A, r, s, p, g, pg0, pg1, tab);
+  else run_unit<KVT, D, false>(P, A, r, s, p, g, pg0, pg1, tab);
   if (nch == 1) {
     finish<KVT, D>(P, A, r, g);
     return;
@@ -967,13 +975,19 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
     hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true>), tiles, dim3(256), 0, st, P);
     return;
   }
+  const dim3 chunk_grid(a.n_rows * ((n_ch + 3) / 4), n_kv);
+  if (chunk && a.k_new && a.distinct) {
+    hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, true>), chunk_grid, dim3(256), 0, st, P);
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units * P.G), dim3(64), 0, st, P);
+    return;
+  }
   if (a.k_new) hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
   const int n_tiles = P.tile_rows > 0 ? (a.n_rows + P.tile_rows - 1) / P.tile_rows : 0;
   if (!chunk) {
     hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false>), tiles, dim3(256), 0, st, P);
     return;
   }
-  hipLaunchKernelGGL((attn_chunked_kernel<KVT, D>), dim3(a.n_rows * ((n_ch + 3) / 4), n_kv), dim3(256), 0, st, P);
+  hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), chunk_grid, dim3(256), 0, st, P);
   if (n_tiles)
     hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB>), dim3(n_tiles * n_ch, n_kv), dim3(64), 0, st, P, n_ch);
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units * P.G), dim3(64), 0, st, P);

@@ -87,15 +87,16 @@ FUSED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("chunk", [8, 2])
 @pytest.mark.parametrize("kvt,nq,nkv,d", FUSED_CASES)
-def test_fused_append_bit_identical(H, kvt, nq, nkv, d):
+def test_fused_append_bit_identical(H, kvt, nq, nkv, d, chunk):
     """With every sequence appearing once, the append runs inside the attention
     kernel (the row's token substituted in registers).  Outputs and the pool
     bytes it leaves are bit-identical to the separate append followed by
     attention, for a token in every one of the 32 page slots."""
     lens = tuple(range(1, 41)) + (63, 64, 65, 96, 97, 128, 129)
     w = wl.make("attn", "cpu", seed=40 + nq + d + kvt, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens,
-                append=True, chunk=8)
+                append=True, chunk=chunk)  # 8: one chunk per row; 2: the row's last chunk appends
     dev = lambda t: t.to("cuda")
     outs, pools = [], []
     for distinct in (False, True):
@@ -379,3 +380,25 @@ def test_full_tables(H, orc, kvt, chunk):
         e = H.rel_err(out.cpu().numpy(), want)
         print(f"full tables kv{kvt} chunk {chunk} distinct={distinct}: {e:.2e}")
         assert e <= TOL_F32_OUT
+
+
+@pytest.mark.parametrize("chunk", [100, 80])
+def test_fused_append_long_rows(H, orc, chunk):
+    """The fused append for rows whose own page lies 64 or more pages past the
+    start of the wave's page range (2,100- and 2,600-token contexts): outputs
+    and pool bytes equal the separate append's, and the oracle's."""
+    import paged_kv_decode_attn_amd as pkd
+    lens = (2600, 33, 2100)
+    w = wl.make("attn", "cpu", seed=77, n_q=4, n_kv=2, d=128, kv_dtype=wl.BF16, lens=lens, append=True,
+                chunk=chunk, extra_pages=0)
+    outs, pools = [], []
+    for distinct in (False, True):
+        pool = H.GpuPool(w)
+        outs.append(H.run_attention(pool, w.seq, w.pos, w.q.cuda(), w.k_new.cuda(), w.v_new.cuda(), wl.F32,
+                                    distinct=distinct).cpu())
+        pkd.pkd_pool_check(pool.handle)
+        pools.append(pool.pages_bytes().cpu())
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    assert torch.equal(pools[0], pools[1])
+    want = oracle_attn(orc, w, w.seq, w.pos, w.q, w.k_new, w.v_new)
+    assert H.rel_err(outs[1].numpy(), want) <= TOL_F32_OUT
