@@ -26,7 +26,7 @@
  *    without running out of cache": admission refuses with a typed reason and
  *    the numbers).  Host-visible arguments are validated before anything is
  *    launched; on refusal nothing is launched and nothing is modified.
- *  - All device pointers must be 16-byte aligned.
+ *  - Device pointers must be 16-byte aligned unless a call states otherwise.
  *  - Determinism: the output of a row depends only on that row's inputs, its
  *    sequence's pages, the weights and the fixed configuration of the pool or
  *    matrix.  It is bit-identical in any batch, at any position in the batch
