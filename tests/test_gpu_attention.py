@@ -402,3 +402,48 @@ def test_fused_append_long_rows(H, orc, chunk):
     assert torch.equal(pools[0], pools[1])
     want = oracle_attn(orc, w, w.seq, w.pos, w.q, w.k_new, w.v_new)
     assert H.rel_err(outs[1].numpy(), want) <= TOL_F32_OUT
+
+
+def _random_attention_cases(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kvt = int(rng.choice([wl.F32, wl.BF16, wl.FP8], p=[0.2, 0.5, 0.3]))
+        d = int(rng.choice([64, 128]))
+        nkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 7, 8, 16]))
+        n_seq = int(rng.integers(1, 6))
+        lens = tuple(int(v) for v in rng.choice([1, 2, 31, 32, 33, 200, 700, 2100, 2900], size=n_seq))
+        chunk = int(rng.choice([1, 2, 3, 8, 64, 100]))
+        extra = int(rng.integers(0, 3))
+        cases.append((i, kvt, d, nkv, G, lens, chunk, extra))
+    return cases
+
+
+@pytest.mark.parametrize("i,kvt,d,nkv,G,lens,chunk,extra", _random_attention_cases())
+def test_attention_randomized(H, orc, i, kvt, d, nkv, G, lens, chunk, extra):
+    """Seeded random geometries (dtype, head dim, GQA group, context lengths up
+    to 2,900 tokens, page chunk, spare pages): oracle parity with the append,
+    the fused append bit-identical to the separate one, and a shuffled batch
+    bit-identical row by row."""
+    import paged_kv_decode_attn_amd as pkd
+    w = wl.make("attn", "cpu", seed=500 + i, n_q=G * nkv, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens, append=True,
+                chunk=chunk, extra_pages=extra)
+    print(f"case {i}: kv{kvt} d{d} G{G} n_kv{nkv} lens={lens} chunk={chunk} extra={extra}", flush=True)
+    outs, pools = [], []
+    for distinct in (False, True):
+        pool = H.GpuPool(w)
+        outs.append(H.run_attention(pool, w.seq, w.pos, w.q.cuda(), w.k_new.cuda(), w.v_new.cuda(), wl.F32,
+                                    distinct=distinct).cpu())
+        pkd.pkd_pool_check(pool.handle)
+        pools.append(pool.pages_bytes().cpu())
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    assert torch.equal(pools[0], pools[1])
+    want = oracle_attn(orc, w, w.seq, w.pos, w.q, w.k_new, w.v_new)
+    e = H.rel_err(outs[0].numpy(), want)
+    assert e <= TOL_F32_OUT, e
+    perm = np.random.default_rng(i).permutation(w.n_rows)
+    pool = H.GpuPool(w)
+    sh = H.run_attention(pool, w.seq[perm], w.pos[perm], w.q[perm].cuda(), w.k_new[perm].cuda(),
+                         w.v_new[perm].cuda(), wl.F32, distinct=True).cpu()
+    assert torch.equal(sh.view(torch.int32), outs[0][torch.as_tensor(perm)].view(torch.int32))
