@@ -447,3 +447,44 @@ def test_attention_randomized(H, orc, i, kvt, d, nkv, G, lens, chunk, extra):
     sh = H.run_attention(pool, w.seq[perm], w.pos[perm], w.q[perm].cuda(), w.k_new[perm].cuda(),
                          w.v_new[perm].cuda(), wl.F32, distinct=True).cpu()
     assert torch.equal(sh.view(torch.int32), outs[0][torch.as_tensor(perm)].view(torch.int32))
+
+
+def _random_tile_cases(n=6, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kvt = int(rng.choice([wl.F32, wl.BF16, wl.FP8]))
+        d = int(rng.choice([64, 128]))
+        nkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 3, 5, 7, 16]))
+        chunk = int(rng.choice([1, 2, 5, 8, 16]))
+        p0 = int(rng.integers(1000, 2200))
+        n_slice = int(rng.integers(128, 260))
+        lead = int(rng.integers(0, 5))  # decode rows before the slice (shifts it off the tile grid)
+        out.append((i, kvt, d, nkv, G, chunk, p0, n_slice, lead))
+    return out
+
+
+@pytest.mark.parametrize("i,kvt,d,nkv,G,chunk,p0,n_slice,lead", _random_tile_cases())
+def test_prefill_tiles_randomized(H, orc, i, kvt, d, nkv, G, chunk, p0, n_slice, lead):
+    """Seeded random prompt slices read as shared tiles (odd G, every pool
+    dtype, random chunk sizes and offsets): bit-identical to the per-row
+    kernels and within the oracle's tolerance."""
+    lens = (p0 + n_slice + 40,) + tuple(range(40, 40 + 30 * lead, 30))
+    w = wl.make("attn", "cpu", seed=900 + i, n_q=G * nkv, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens, append=True,
+                chunk=chunk, extra_pages=1)
+    gen = torch.Generator().manual_seed(901 + i)
+    qd = wl.F32 if kvt == wl.F32 else wl.BF16
+    seq = np.concatenate([np.arange(1, 1 + lead), np.zeros(n_slice)]).astype(np.int32)
+    pos = np.concatenate([np.asarray(lens[1:], np.int32) - 1, np.arange(p0, p0 + n_slice)]).astype(np.int32)
+    n = seq.size
+    q = wl.encode(torch.randn((n, G * nkv, d), generator=gen), qd)
+    kn = wl.encode(torch.randn((n, nkv, d), generator=gen), qd)
+    vn = wl.encode(torch.randn((n, nkv, d), generator=gen), qd)
+    print(f"tiles case {i}: kv{kvt} d{d} G{G} n_kv{nkv} chunk {chunk} slice {p0}+{n_slice} lead {lead}", flush=True)
+    pool = H.GpuPool(w)
+    out = H.run_attention(pool, seq, pos, q.cuda(), kn.cuda(), vn.cuda()).cpu()
+    ref = H.run_attention(pool, seq, pos, q.cuda(), None, None, distinct=True).cpu()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    want = oracle_attn(orc, w, seq, pos, q, kn, vn)
+    assert H.rel_err(out.numpy(), want) <= TOL_F32_OUT
