@@ -84,7 +84,12 @@ __device__ __forceinline__ void load_x(const uint8_t* x, int64_t stride, int r, 
       f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + i);
       out[i] = v[0]; out[i + 1] = v[1]; out[i + 2] = v[2]; out[i + 3] = v[3];
     }
+  } else if constexpr (E == 4) {
+    // f32 weights (4 per 16-byte vector) against bf16 activations: 8 bytes
+    const u32x2 v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(x) + (int64_t)r * stride + k);
+    out[0] = bf16lo(v.x); out[1] = bf16hi(v.x); out[2] = bf16lo(v.y); out[3] = bf16hi(v.y);
   } else {
+    static_assert(E % 8 == 0, "bf16 activations come in 8-element vectors");
     const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + (int64_t)r * stride + k;
 #pragma unroll
     for (int i = 0; i < E; i += 8) {

@@ -80,6 +80,9 @@ GEMV_CASES = [
     (wl.BF16, wl.BF16, 260, 18944, 5, False, True, wl.F32),
     (wl.F32, wl.F32, 512, 256, 4, False, False, wl.F32),
     (wl.F32, wl.F32, 256, 256, 37, False, True, wl.F32),
+    # f32 weights against bf16 activations (4-element activation vectors)
+    (wl.F32, wl.BF16, 9000, 3584, 3, True, False, wl.F32),
+    (wl.F32, wl.BF16, 700, 192, 17, False, True, wl.BF16),
     (wl.FP8, wl.BF16, 300, 3584, 2, False, False, wl.F32),
     (wl.FP8, wl.F32, 2 * 64, 1024, 9, True, False, wl.BF16),
     # enough row groups (>= 8192) that K is not split across a block's waves
@@ -408,3 +411,88 @@ def test_epilogue_row_scale_and_rope(H, orc, fam, wdt, xdt, rows, cols, n, S, si
     e = H.rel_err(y.cpu().numpy(), want)
     print(f"epilogue fam{fam} w{wdt} {rows}x{cols} n={n} S={S} silu={silu}: {e:.2e}")
     assert e <= TOL
+
+
+def _random_proj_cases(count=14, seed=314):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        fam = int(rng.choice([0, 1, 2, 3]))
+        wdt = int(rng.choice([wl.F32, wl.BF16, wl.FP8]))
+        xdt = int(rng.choice([wl.F32, wl.BF16]))
+        if fam in (1, 2, 3) and wdt == wl.F32:
+            continue
+        if fam == 2 and wdt != wl.FP8:
+            continue
+        if (fam == 3 or (fam == 1 and wdt == wl.BF16)) and xdt != wl.BF16:
+            continue
+        silu = bool(rng.random() < 0.3)
+        rows = int(rng.choice([128, 256, 384, 640, 4096, 9000]))
+        if fam in (1, 2):
+            rows = (rows + 127) // 128 * 128
+        if silu:
+            rows = rows // 2 * 2
+        cols = int(rng.choice([128, 256, 1024, 2048, 3584]))
+        n = int(rng.choice([1, 3, 16, 17, 100, 300]))
+        S = int(rng.choice([1, 2, 3])) if fam in (1, 2) else 1
+        if fam in (1, 2):
+            S = min(S, cols // (128 if fam == 2 else 64))  # at least one K block per split
+        res = bool(not silu and rng.random() < 0.4)
+        scaled = bool(rng.random() < 0.5)
+        rope = bool(not silu and rng.random() < 0.5)
+        out.append((len(out), fam, wdt, xdt, rows, cols, n, silu, res, S, scaled, rope))
+    return out
+
+
+@pytest.mark.parametrize("i,fam,wdt,xdt,rows,cols,n,silu,res,S,scaled,rope", _random_proj_cases())
+def test_projection_randomized(H, orc, i, fam, wdt, xdt, rows, cols, n, silu, res, S, scaled, rope):
+    """Seeded random projections over every family, dtype pair, shape, batch,
+    K split and epilogue (residual, silu pair, per-row factor, rotary pairs):
+    oracle parity, and the first rows alone give their bits in the batch."""
+    import paged_kv_decode_attn_amd as pkd
+    seed = 1000 + i
+    W, s = make_w(rows, cols, wdt, seed)
+    x = make_x(n, cols, xdt, seed)
+    g = torch.Generator().manual_seed(seed)
+    nout = rows // 2 if silu else rows
+    residual = torch.randn((n, rows), generator=g) if res else None
+    rsc = (0.5 + torch.rand(n, generator=g)).float() if scaled else None
+    hd = 64
+    rcols = (nout // hd) * hd if rope else 0
+    pos = torch.randint(0, 4000, (n,), generator=g, dtype=torch.int32)
+    Wd = W.cuda()
+    M = pkd.make_matrix(Wd, rows, cols, wdt, s, fam, S)
+    cs = torch.empty((n, hd // 2, 2), device="cuda")
+    if rope:
+        pkd.rope_table(pos.cuda(), n, hd, 10000.0, cs)
+    wsb = pkd.pkd_gemv_workspace_bytes(M, n)
+    ws = H.aligned_empty(wsb) if wsb else None
+    print(f"proj case {i}: family {fam} w{wdt} x{xdt} {rows}x{cols} n={n} silu={silu} res={res} S={S} "
+          f"scaled={scaled} rope={rope}", flush=True)
+
+    def run(m):
+        y = torch.empty((m, nout), device="cuda")
+        pkd.gemv_rows(M, x[:m].contiguous().cuda(), xdt, m, y, wl.F32,
+                      None if residual is None else residual[:m].contiguous().cuda(), silu, None, ws,
+                      row_scale=None if rsc is None else rsc[:m].contiguous().cuda(),
+                      rope_cs=cs[:m].contiguous() if rope and rcols else None, rope_cols=rcols, rope_head_dim=hd)
+        torch.cuda.synchronize()
+        return y.cpu()
+    y = run(n)
+    raw = oracle_proj(orc, W, wdt, s, x, xdt, 1 if (fam in (1, 2) and wdt == wl.FP8) else 0)
+    if rsc is not None:
+        raw = raw * rsc.numpy().astype(np.float64)[:, None]
+    if silu:
+        F = rows // 2
+        want = raw[:, :F] / (1 + np.exp(-raw[:, :F])) * raw[:, F:]
+    else:
+        want = raw.copy()
+        if rcols:
+            want[:, :rcols] = orc.rope_rows(raw[:, :rcols], rcols // hd, hd, pos.numpy(), 10000.0)
+        if residual is not None:
+            want = want + residual.numpy().astype(np.float64)
+    e = H.rel_err(y.numpy(), want)
+    print(f"  rel err {e:.2e}", flush=True)
+    assert e <= TOL
+    m = min(n, 2)
+    assert torch.equal(run(m).view(torch.int32), y[:m].view(torch.int32))
