@@ -155,6 +155,11 @@ typedef struct {
   size_t table_offset;
   size_t counts_offset;
   size_t error_offset;
+  int64_t shared_pages; /* host count: physical pages that two or more sequences' block
+                           tables list (a shared prompt prefix).  While it is 0 the
+                           attention kernels look for no shared pages to stage, which
+                           leaves them more waves per compute unit; results are the
+                           same either way. */
 } pkd_pool_info;
 
 /* Bytes kv_pool_create needs for `desc`, computed without allocating; 0 if
@@ -193,7 +198,9 @@ pkd_status pkd_pool_info_get(const pkd_pool* pool, pkd_pool_info* info);
  * above max_pages_per_seq {needed = count, available = max_pages_per_seq} or
  * a page id outside [0, num_pages) {needed = id, available = num_pages};
  * PKD_ERR_DUPLICATE_PAGE for a page listed twice in one sequence.
- * Synchronous: returns after the table has reached the device.
+ * Synchronous: reads back the tables it replaces (to keep the per-page
+ * sequence counts behind pkd_pool_info.shared_pages), writes the new ones and
+ * returns after they have reached the device.
  */
 pkd_status block_table_set(pkd_pool* pool, int32_t first_seq, int32_t n_seqs,
                            const int32_t* pages_host, const int32_t* n_pages_host,

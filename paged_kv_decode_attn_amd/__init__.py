@@ -48,7 +48,8 @@ class pkd_pool_desc(ctypes.Structure):
 class pkd_pool_info(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("pages_offset", ctypes.c_size_t),
                 ("block_bytes", ctypes.c_size_t), ("table_offset", ctypes.c_size_t),
-                ("counts_offset", ctypes.c_size_t), ("error_offset", ctypes.c_size_t)]
+                ("counts_offset", ctypes.c_size_t), ("error_offset", ctypes.c_size_t),
+                ("shared_pages", ctypes.c_int64)]
 
 
 ROWS_DISTINCT_SEQS = 1

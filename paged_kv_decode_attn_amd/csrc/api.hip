@@ -219,6 +219,11 @@ pkd_status kv_pool_create(const pkd_pool_desc* desc, void* dev_mem, size_t bytes
                 "pool needs %zu bytes, buffer has %zu", info.total_bytes, bytes);
   pkd_pool* p = (pkd_pool*)calloc(1, sizeof(pkd_pool));
   if (!p) return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)sizeof(pkd_pool), 0, "host allocation of the handle failed");
+  p->page_refs = (int32_t*)calloc((size_t)desc->num_pages, sizeof(int32_t));
+  if (!p->page_refs) {
+    free(p);
+    return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)desc->num_pages * 4, 0, "host allocation of page counts failed");
+  }
   p->desc = *desc;
   p->base = (uint8_t*)dev_mem;
   p->bytes = bytes;
@@ -232,6 +237,7 @@ pkd_status kv_pool_create(const pkd_pool_desc* desc, void* dev_mem, size_t bytes
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, (int32_t*)(p->base + info.error_offset), 64, 0);
   pkd_status s = check_launch(err, "kv_pool_create");
   if (s != PKD_OK) {
+    free(p->page_refs);
     free(p);
     return s;
   }
@@ -240,6 +246,7 @@ pkd_status kv_pool_create(const pkd_pool_desc* desc, void* dev_mem, size_t bytes
 }
 
 pkd_status kv_pool_destroy(pkd_pool* pool) {
+  if (pool) free(pool->page_refs);
   free(pool);
   return PKD_OK;
 }
@@ -247,6 +254,7 @@ pkd_status kv_pool_destroy(pkd_pool* pool) {
 pkd_status pkd_pool_info_get(const pkd_pool* pool, pkd_pool_info* info) {
   if (!pool || !info) return PKD_ERR_INVALID_ARG;
   *info = pool->info;
+  info->shared_pages = pool->shared_pages;
   return PKD_OK;
 }
 
@@ -282,11 +290,25 @@ pkd_status block_table_set(pkd_pool* pool, int32_t first_seq, int32_t n_seqs, co
   hipStream_t st = (hipStream_t)stream;
   int32_t* dt = (int32_t*)(pool->base + pool->info.table_offset) + (size_t)first_seq * mp;
   int32_t* dc = (int32_t*)(pool->base + pool->info.counts_offset) + first_seq;
-  hipError_t e = hipMemcpyAsync(dt, table.data(), sizeof(int32_t) * table.size(), hipMemcpyHostToDevice, st);
+  // the tables being replaced, to keep the per-page sequence counts exact
+  std::vector<int32_t> old_table(table.size()), old_counts((size_t)n_seqs);
+  hipError_t e = hipMemcpyAsync(old_table.data(), dt, sizeof(int32_t) * table.size(), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(old_counts.data(), dc, sizeof(int32_t) * (size_t)n_seqs, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipMemcpyAsync(dt, table.data(), sizeof(int32_t) * table.size(), hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
     e = hipMemcpyAsync(dc, n_pages_host, sizeof(int32_t) * (size_t)n_seqs, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(err, PKD_ERR_DEVICE, 0, 0, "block_table_set: %s", hipGetErrorString(e));
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    for (int32_t j = 0; j < old_counts[i] && j < mp; ++j) {
+      const int32_t pg = old_table[(size_t)i * mp + j];
+      if (pg >= 0 && pg < d.num_pages && pool->page_refs[pg] > 0 && --pool->page_refs[pg] == 1) --pool->shared_pages;
+    }
+    for (int32_t j = 0; j < n_pages_host[i]; ++j)
+      if (++pool->page_refs[table[(size_t)i * mp + j]] == 2) ++pool->shared_pages;
+  }
   return ok(err);
 }
 

@@ -610,19 +610,16 @@ struct Stage {
   static constexpr int BYTES = PAGES * 2 * BLOCK;            // at most 32 KiB
 };
 
-template <int KVT, int D, bool FUSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_direct_kernel(AttnParams P) {
+// Stages into `stage_mem` the leading pages that every valid row of the
+// workgroup shares, and returns how many there are.  Each wave passes its
+// row's position p, first table window tab and validity ok.  Holds the
+// workgroup's only barriers, reached by all four waves.
+template <int KVT, int D>
+__device__ __forceinline__ int stage_shared(const AttnParams& P, int g, int p, int tab, bool ok,
+                                            uint8_t* stage_mem) {
   using ST = Stage<KVT, D>;
-  __shared__ __attribute__((aligned(16))) uint8_t stage_mem[ST::BYTES];
   __shared__ int meta[4][2 + ST::PAGES];  // per wave: valid, page count, first table entries
   const int wave = threadIdx.x >> 6, l = lane_id();
-  const int r = blockIdx.x * 4 + wave, g = blockIdx.y;
-  // rows of a shared tile are attn_tile_kernel's: treated here as absent
-  const bool in_range = r < P.n_rows && !(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows));
-  const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
-  int count, tab;
-  row_meta(P, s, count, tab);
-  const bool ok = in_range && row_ok(P, s, p, count, g == 0);
   if (l < ST::PAGES) meta[wave][2 + l] = tab;
   if (l == 0) {
     meta[wave][0] = ok ? 1 : 0;
@@ -649,10 +646,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       break;
     }
   }
-  lds_u8* staged = (lds_u8*)stage_mem;
   if (n_staged > 0) {
     // 1 KiB wave loads: page j, block c, part i; dealt round-robin to the waves
     constexpr int PARTS = ST::BLOCK / 1024;
+    lds_u8* staged = (lds_u8*)stage_mem;
     const uint8_t* gbase = P.pages + (uint64_t)g * 2 * P.block_bytes;
     for (int q = wave; q < n_staged * 2 * PARTS; q += 4) {
       const int j = q / (2 * PARTS), c = (q / PARTS) % 2, i = q % PARTS;
@@ -661,6 +658,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  }
+  return n_staged;
+}
+
+// STAGE: the pool has pages listed by two or more sequences (a shared prompt
+// prefix), so the workgroup looks for leading pages its rows share and stages
+// them in LDS.  Without shared pages the kernel holds no LDS and no barrier,
+// and more waves fit on a CU.  A staged page is read byte for byte as its
+// global copy, so both variants give identical results.
+template <int KVT, int D, bool FUSE, bool STAGE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_direct_kernel(AttnParams P) {
+  using ST = Stage<KVT, D>;
+  const int wave = threadIdx.x >> 6;
+  const int r = blockIdx.x * 4 + wave, g = blockIdx.y;
+  // rows of a shared tile are attn_tile_kernel's: treated here as absent
+  const bool in_range = r < P.n_rows && !(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows));
+  const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
+  int count, tab;
+  row_meta(P, s, count, tab);
+  const bool ok = in_range && row_ok(P, s, p, count, g == 0);
+  int n_staged = 0;
+  const lds_u8* staged = nullptr;
+  if constexpr (STAGE) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage_mem[ST::BYTES];
+    n_staged = stage_shared<KVT, D>(P, g, p, tab, ok, stage_mem);
+    staged = (const lds_u8*)stage_mem;
   }
   if (!in_range) return;
   if (!ok) {
@@ -967,12 +990,13 @@ static int tile_rows_for(int kvt, int G) { return (kvt == PKD_F32 ? 1 : 2) * (16
 
 template <int KVT, int D>
 static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk, int n_ch,
-                       hipStream_t st) {
+                       bool stage, hipStream_t st) {
   constexpr int NB = KVT == 0 ? 1 : 2;
   const int units = a.n_rows * n_kv;
   const dim3 tiles((a.n_rows + 3) / 4, n_kv);  // direct mode: four rows of one kv head per workgroup
   if (!chunk && a.k_new && a.distinct) {
-    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true>), tiles, dim3(256), 0, st, P);
+    if (stage) hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true, true>), tiles, dim3(256), 0, st, P);
+    else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true, false>), tiles, dim3(256), 0, st, P);
     return;
   }
   const dim3 chunk_grid(a.n_rows * ((n_ch + 3) / 4), n_kv);
@@ -984,7 +1008,8 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
   if (a.k_new) hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
   const int n_tiles = P.tile_rows > 0 ? (a.n_rows + P.tile_rows - 1) / P.tile_rows : 0;
   if (!chunk) {
-    hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false>), tiles, dim3(256), 0, st, P);
+    if (stage) hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false, true>), tiles, dim3(256), 0, st, P);
+    else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false, false>), tiles, dim3(256), 0, st, P);
     return;
   }
   hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), chunk_grid, dim3(256), 0, st, P);
@@ -1046,14 +1071,16 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   // rows of one sequence.
   constexpr int kTileMinRows = 128;
   P.tile_rows = (a.distinct || !ch || a.n_rows < kTileMinRows) ? 0 : tile_rows_for(kvt, P.G);
+  // leading-page staging only where some page is listed by two sequences
+  const bool stage = pool->shared_pages > 0;
   if (d.head_dim == 128) {
-    if (kvt == PKD_F32) launch_all<0, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
-    else if (kvt == PKD_BF16) launch_all<1, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
-    else launch_all<2, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
+    if (kvt == PKD_F32) launch_all<0, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stage, stream);
+    else if (kvt == PKD_BF16) launch_all<1, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stage, stream);
+    else launch_all<2, 128>(P, a, w, d.num_kv_heads, ch, n_ch, stage, stream);
   } else {
-    if (kvt == PKD_F32) launch_all<0, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
-    else if (kvt == PKD_BF16) launch_all<1, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
-    else launch_all<2, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stream);
+    if (kvt == PKD_F32) launch_all<0, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stage, stream);
+    else if (kvt == PKD_BF16) launch_all<1, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stage, stream);
+    else launch_all<2, 64>(P, a, w, d.num_kv_heads, ch, n_ch, stage, stream);
   }
   return check_launch(err, "paged attention");
 }

@@ -86,6 +86,8 @@ struct pkd_pool {
   size_t bytes;
   pkd_pool_info info;
   int device;
+  int32_t* page_refs;    // host: sequences whose block table lists each physical page
+  int64_t shared_pages;  // pages listed by two or more sequences
 };
 
 namespace pkd {
