@@ -291,6 +291,17 @@ struct Acc {
 // least 1).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// O *= alpha, skipped when no head's maximum moved (alpha == 1 in every lane:
+// the product would leave every bit as it is).  After the first pages the
+// running maximum seldom moves, so most pages skip the multiplies.
+template <int KVT, int D>
+__device__ __forceinline__ void rescale(Acc<KVT, D>& A, float alpha) {
+  using GE = Geo<KVT, D>;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) == 0) return;
+#pragma unroll
+  for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] *= alpha;
+}
+
 // Online-softmax update of one page from its scores; returns the weights p.
 template <int KVT, int D>
 __device__ __forceinline__ void page_softmax(const AttnParams& P, Acc<KVT, D>& A, const f32x4_t (&S)[2], int pg,
@@ -322,8 +333,7 @@ __device__ __forceinline__ void page_softmax(const AttnParams& P, Acc<KVT, D>& A
     }
   A.l = A.l * alpha + ls;
   A.m = m_new;
-#pragma unroll
-  for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] *= alpha;
+  rescale<KVT, D>(A, alpha);
 }
 
 // The same update when a column may have no valid token in the page, or in
@@ -364,8 +374,7 @@ __device__ __forceinline__ void page_softmax_masked(const AttnParams& P, Acc<KVT
     }
   A.l = A.l * alpha + ls;
   A.m = m_new;
-#pragma unroll
-  for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] *= alpha;
+  rescale<KVT, D>(A, alpha);
 }
 
 template <int KVT, int D>
