@@ -676,11 +676,16 @@ __device__ __forceinline__ int stage_shared(const AttnParams& P, int g, int p, i
 // them in LDS.  Without shared pages the kernel holds no LDS and no barrier,
 // and more waves fit on a CU.  A staged page is read byte for byte as its
 // global copy, so both variants give identical results.
+//   Grid: with STAGE, (row quads) x kv heads, so that a workgroup holds four
+//   rows of one kv head; without, units u = row * n_kv + kv head dealt four
+//   to a workgroup, so that the kv heads of a row, whose blocks lie side by
+//   side in each page, are read together.
 template <int KVT, int D, bool FUSE, bool STAGE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_direct_kernel(AttnParams P) {
   using ST = Stage<KVT, D>;
   const int wave = threadIdx.x >> 6;
-  const int r = blockIdx.x * 4 + wave, g = blockIdx.y;
+  const int u = blockIdx.x * 4 + wave;
+  const int r = STAGE ? u : u / P.n_kv, g = STAGE ? (int)blockIdx.y : u % P.n_kv;
   // rows of a shared tile are attn_tile_kernel's: treated here as absent
   const bool in_range = r < P.n_rows && !(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows));
   const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
@@ -1002,10 +1007,11 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
                        bool stage, hipStream_t st) {
   constexpr int NB = KVT == 0 ? 1 : 2;
   const int units = a.n_rows * n_kv;
-  const dim3 tiles((a.n_rows + 3) / 4, n_kv);  // direct mode: four rows of one kv head per workgroup
+  const dim3 tiles((a.n_rows + 3) / 4, n_kv);  // direct mode, staging: four rows of one kv head per workgroup
+  const dim3 quads((units + 3) / 4);          // direct mode: four (row, kv head) units per workgroup
   if (!chunk && a.k_new && a.distinct) {
     if (stage) hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true, true>), tiles, dim3(256), 0, st, P);
-    else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true, false>), tiles, dim3(256), 0, st, P);
+    else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true, false>), quads, dim3(256), 0, st, P);
     return;
   }
   const dim3 chunk_grid(a.n_rows * ((n_ch + 3) / 4), n_kv);
@@ -1018,7 +1024,7 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
   const int n_tiles = P.tile_rows > 0 ? (a.n_rows + P.tile_rows - 1) / P.tile_rows : 0;
   if (!chunk) {
     if (stage) hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false, true>), tiles, dim3(256), 0, st, P);
-    else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false, false>), tiles, dim3(256), 0, st, P);
+    else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false, false>), quads, dim3(256), 0, st, P);
     return;
   }
   hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), chunk_grid, dim3(256), 0, st, P);
