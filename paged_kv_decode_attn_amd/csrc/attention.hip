@@ -725,12 +725,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int cw = (P.max_ch + 3) / 4;
   const int r = blockIdx.x / cw, c = 4 * (blockIdx.x % cw) + (threadIdx.x >> 6), g = blockIdx.y;
   if (c >= P.max_ch) return;
-  if (P.tile_rows > 0 && tile_shared(P, r / P.tile_rows)) return;
   const int l = lane_id(), grp = l >> 4, n = l & 15;
   const int s = P.seq[r], p = P.pos[r];
+  const int npg = (p + kPage) / kPage;
+  // chunks past the row's context (most waves of a batch of short rows) leave
+  // after this one load; chunk 0 stays to report a refused row
+  if (c > 0 && c * P.chunk_pages >= npg) return;
+  if (P.tile_rows > 0 && tile_shared(P, r / P.tile_rows)) return;
   const int count = (s >= 0 && s < P.max_seqs) ? P.counts[s] : 0;
   if (!row_ok(P, s, p, count, c == 0 && g == 0)) return;
-  const int npg = (p + kPage) / kPage;
   const int nch = (npg + P.chunk_pages - 1) / P.chunk_pages;
   if (c >= nch) return;
   const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
