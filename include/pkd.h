@@ -27,6 +27,10 @@
  *    the numbers).  Host-visible arguments are validated before anything is
  *    launched; on refusal nothing is launched and nothing is modified.
  *  - Device pointers must be 16-byte aligned unless a call states otherwise.
+ *  - Threads: calls on different pools, or calls that only read a pool
+ *    (attention, decode_step, pkd_pool_info_get), may run from several host
+ *    threads at once.  block_table_set and kv_pool_destroy change a pool's
+ *    host state and must not overlap any other call on the same pool.
  *  - Determinism: the output of a row depends only on that row's inputs, its
  *    sequence's pages, the weights and the fixed configuration of the pool or
  *    matrix.  It is bit-identical in any batch, at any position in the batch

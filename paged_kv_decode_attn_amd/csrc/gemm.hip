@@ -26,6 +26,8 @@
 // depend on S (a per-matrix constant) but never on the batch.  Work items are
 // dealt so that an XCD runs a contiguous run of tiles sharing a weight block.
 
+#include <atomic>
+
 #include "common.h"
 
 namespace pkd {
@@ -578,10 +580,15 @@ pkd_status gemv_launch(const ProjArgs& a, hipStream_t stream, pkd_error* err);
 template <int MODE, int TM>
 static void launch_tile(const GemmParams& P, int grid, hipStream_t stream) {
   constexpr int lds = Tile<MODE, TM>::LDS_BYTES;
-  static bool attr = false;  // dynamic LDS above 64 KiB must be enabled once per kernel
-  if (!attr) {
+  // dynamic LDS above 64 KiB must be enabled once per kernel and device; two
+  // threads may both enable it, which is harmless
+  static std::atomic<uint64_t> enabled{0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(enabled.load(std::memory_order_acquire) & bit)) {
     (void)hipFuncSetAttribute((const void*)gemm_kernel<MODE, TM>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr = true;
+    enabled.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL((gemm_kernel<MODE, TM>), dim3(grid), dim3(64 * NWAVES), lds, stream, P);
 }

@@ -293,6 +293,73 @@ def test_block_table_refusals(H):
     assert torch.equal(out, fresh)
 
 
+def test_shared_page_count(H):
+    """block_table_set keeps the count of physical pages that two or more
+    sequences list (pkd_pool_info.shared_pages) exact as tables are set,
+    replaced and cleared; a refused call leaves it unchanged."""
+    import paged_kv_decode_attn_amd as pkd
+    desc = pkd.pkd_pool_desc(8, 32, 1, 64, wl.BF16, 1.0, 1.0, 3, 4, 4)
+    mem = H.aligned_empty(pkd.pkd_pool_bytes(desc))
+    h = pkd.kv_pool_create(desc, mem)
+    try:
+        def shared():
+            return pkd.pkd_pool_info_get(h).shared_pages
+
+        def put(seq, pages):
+            row = np.full((1, 4), -1, np.int32)
+            row[0, :len(pages)] = pages
+            pkd.block_table_set(h, seq, row, [len(pages)])
+
+        assert shared() == 0
+        put(0, [0, 1, 2])
+        put(1, [0, 1, 3])
+        assert shared() == 2          # pages 0 and 1
+        put(2, [0, 4])
+        assert shared() == 2          # page 0 now listed three times
+        put(1, [5, 6])
+        assert shared() == 1          # page 1 back to one sequence; page 0 still shared
+        with pytest.raises(pkd.PkdError):
+            put(1, [5, 5])            # duplicate in one table: refused, nothing changes
+        assert shared() == 1
+        put(2, [])
+        assert shared() == 0
+        both = np.array([[7, 0, -1, -1], [7, 1, -1, -1]], np.int32)
+        pkd.block_table_set(h, 1, both, [2, 2])
+        assert shared() == 3          # page 7 (sequences 1, 2), 0 (0, 1) and 1 (0, 2)
+    finally:
+        pkd.kv_pool_destroy(h)
+
+
+@pytest.mark.parametrize("kvt,nq,nkv,d,append", [
+    (wl.BF16, 28, 4, 128, True), (wl.FP8, 14, 2, 128, True), (wl.F32, 4, 2, 64, False)])
+def test_staging_variant_bit_identical(H, kvt, nq, nkv, d, append):
+    """The same logical pool with its first pages shared physically (the
+    staging kernel runs) and with private copies of them (the kernel without
+    LDS, whose workgroups take four (row, kv head) units) gives the same bits."""
+    import dataclasses
+    import paged_kv_decode_attn_amd as pkd
+    lens = (40, 50, 70, 100, 33, 64, 65, 129, 97)
+    w = wl.make("attn", "cpu", seed=31 + nq + d + kvt, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens,
+                append=append, chunk=8, shared_first_page=True)
+    tables = w.tables.copy()
+    used = {int(tables[s][j]) for s in range(len(lens)) for j in range(int(w.counts[s]))}
+    free = sorted(set(range(w.num_pages)) - used)
+    k = 0
+    for s in range(1, len(lens)):
+        if tables[s][0] == tables[0][0]:
+            tables[s][0] = free[k]
+            k += 1
+    assert k >= 2
+    w_private = dataclasses.replace(w, tables=tables)
+    pool_shared, pool_private = H.GpuPool(w), H.GpuPool(w_private)
+    assert pkd.pkd_pool_info_get(pool_shared.handle).shared_pages == 1
+    assert pkd.pkd_pool_info_get(pool_private.handle).shared_pages == 0
+    dev = lambda t: None if t is None else t.to("cuda")
+    outs = [H.run_attention(pool, w.seq, w.pos, dev(w.q), dev(w.k_new), dev(w.v_new), wl.F32,
+                            distinct=True).cpu() for pool in (pool_shared, pool_private)]
+    assert torch.equal(outs[0], outs[1])
+
+
 PREFILL_CASES = [
     # (kv dtype, q heads, kv heads, head dim, chunk pages): rows per shared tile = (1 or 2) x 16 / G
     (wl.BF16, 4, 2, 128, 2),    # G 2: tiles of 16 rows
