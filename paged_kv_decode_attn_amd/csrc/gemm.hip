@@ -593,26 +593,35 @@ static void launch_tile(const GemmParams& P, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_kernel<MODE, TM>), dim3(grid), dim3(64 * NWAVES), lds, stream, P);
 }
 
-// Activation tile height: 256 when that still gives every CU a tile, else 128.
-// Either height runs the same k-loop per output, so the choice never changes a
-// result.
+// Measured per-CU rates of the two tile heights at the 7B shapes: the 256-row
+// tile pulls fewer operand bytes per product (131 against 87 flop per byte)
+// and runs at about 4.7 TFLOP/s per CU, the 128-row tile at about 3.5.
+constexpr double kRate256 = 4.7e12, kRate128 = 3.5e12;
+
+// Activation tile height: the one whose rounds of workgroups over the 256 CUs
+// take less time at those rates (a tile's time is proportional to its height
+// over its rate).  Either height runs the same k-loop per output, so the
+// choice never changes a result.
 static int tile_m_for(int tiles_n, int splits, int M) {
-  const int items256 = tiles_n * splits * ((M + 255) / 256);
-  return items256 >= 256 ? 256 : 128;
+  const long i256 = (long)tiles_n * splits * ((M + 255) / 256);
+  const long i128 = (long)tiles_n * splits * ((M + 127) / 128);
+  const double t256 = (double)((i256 + 255) / 256) * 256.0 / kRate256;
+  const double t128 = (double)((i128 + 255) / 256) * 128.0 / kRate128;
+  return t256 <= t128 ? 256 : 128;
 }
 
 
 // Estimated time of a split, in microseconds: rounds of workgroups over the
 // 256 CUs times the time of one workgroup (tile height x 256 weight rows x its
-// share of K, at about 4 TFLOP/s per CU as measured for these tiles), plus the
-// partial sums of S > 1, written once and read once by the finish pass (at
-// about 5 TB/s).  A larger S must beat the best so far by 5%.  With these two
-// terms the model picks the measured best S at the 7B shapes at batch 768
-// (qkv 2, W_o 3, gate/up 1, down 3) and within 5% of it at batch 256 (qkv 4,
-// W_o 6, gate/up 1, down 8).
+// share of K, at the measured rate of that tile height), plus the partial sums
+// of S > 1, written once and read once by the finish pass (at about 5 TB/s).
+// A larger S must beat the best so far by 5%.  With these terms the model
+// picks the measured best S at the 7B shapes at batch 768 (qkv 2, W_o 3,
+// gate/up 1, down 6 on the 256-row tile: 115 us against 130 at S = 3) and at
+// batch 256 (qkv 6, W_o 6, gate/up 1, down 8).
 int suggest_k_splits(int rows, int cols, int family, int typical_rows) {
   if (!tiled_family(family) || rows <= 0 || cols <= 0 || typical_rows <= 0) return 1;
-  constexpr double kFlopsPerCu = 4e12, kPartialBytesPerS = 5e12;
+  constexpr double kPartialBytesPerS = 5e12;
   const int tiles_n = (rows + TN - 1) / TN;
   int best = 1;
   double best_cost = 0;
@@ -620,7 +629,7 @@ int suggest_k_splits(int rows, int cols, int family, int typical_rows) {
     if (s > 1 && cols / s < 512) break;
     const int tm = tile_m_for(tiles_n, s, typical_rows);
     const long items = (long)tiles_n * s * ((typical_rows + tm - 1) / tm);
-    const double wg_us = 2.0 * tm * TN * ((cols + s - 1) / s) / kFlopsPerCu * 1e6;
+    const double wg_us = 2.0 * tm * TN * ((cols + s - 1) / s) / (tm == 256 ? kRate256 : kRate128) * 1e6;
     const double partial_us = s > 1 ? 2.0 * s * rows * (double)typical_rows * 4 / kPartialBytesPerS * 1e6 : 0.0;
     const double cost = (double)((items + 255) / 256) * wg_us + partial_us;
     if (s == 1 || cost < 0.95 * best_cost) {
