@@ -464,7 +464,9 @@ __device__ __forceinline__ void append_store(const AttnParams& P, int g, int pag
   }
 }
 
-// Runs pages [pg0, pg1) of row r, kv head g.  One K and one V block live in
+// Runs pages [pg0, pg1) of row r, kv head g, with the row's query registers
+// qv / qf (load_q; callers issue that load early, since it depends on the row
+// and kv head alone).  One K and one V block live in
 // registers: the next page's K is requested as soon as the score products have
 // consumed the current K, and its V once the P.V products have consumed the
 // current V, so a wave keeps about one page in flight with half the registers
@@ -475,12 +477,10 @@ __device__ __forceinline__ void append_store(const AttnParams& P, int g, int pag
 // are read from there, byte for byte what the global loads would return.
 template <int KVT, int D, bool FUSE = false>
 __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, int r, int s, int p_row, int g,
-                                         int pg0, int pg1, int tab, const lds_u8* staged = nullptr,
+                                         int pg0, int pg1, int tab, const QRegs<KVT, D>& qv,
+                                         const QFRegs<KVT, D>& qf, const lds_u8* staged = nullptr,
                                          int n_staged = 0) {
   using GE = Geo<KVT, D>;
-  u32x4 qv[GE::NQ];
-  float qf[GE::NQ];
-  load_q<KVT, D>(P, r, g, qv, qf);
 #pragma unroll
   for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   A.m = -INFINITY;
@@ -686,6 +686,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const int wave = threadIdx.x >> 6;
   const int u = blockIdx.x * 4 + wave;
   const int r = STAGE ? u : u / P.n_kv, g = STAGE ? (int)blockIdx.y : u % P.n_kv;
+  // the query depends on the row and kv head alone: requested first, so that
+  // it arrives while the row's metadata and any staged pages are read
+  u32x4 qv[Geo<KVT, D>::NQ];
+  float qf[Geo<KVT, D>::NQ];
+  load_q<KVT, D>(P, r < P.n_rows ? r : 0, g, qv, qf);
   // rows of a shared tile are attn_tile_kernel's: treated here as absent
   const bool in_range = r < P.n_rows && !(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows));
   const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     return;
   }
   Acc<KVT, D> A;
-  run_unit<KVT, D, FUSE>(P, A, r, s, p, g, 0, (p + kPage) / kPage, tab, staged, n_staged);
+  run_unit<KVT, D, FUSE>(P, A, r, s, p, g, 0, (p + kPage) / kPage, tab, qv, qf, staged, n_staged);
   finish<KVT, D>(P, A, r, g);
 }
 
@@ -731,6 +736,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // chunks past the row's context (most waves of a batch of short rows) leave
   // after this one load; chunk 0 stays to report a refused row
   if (c > 0 && c * P.chunk_pages >= npg) return;
+  u32x4 qv[GE::NQ];
+  float qf[GE::NQ];
+  load_q<KVT, D>(P, r, g, qv, qf);
   if (P.tile_rows > 0 && tile_shared(P, r / P.tile_rows)) return;
   const int count = (s >= 0 && s < P.max_seqs) ? P.counts[s] : 0;
   if (!row_ok(P, s, p, count, c == 0 && g == 0)) return;
@@ -739,8 +747,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
   const int tab = pg0 + l < pg1 ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
   Acc<KVT, D> A;
-  if (FUSE && c == nch - 1) run_unit<KVT, D, true>(P, A, r, s, p, g, pg0, pg1, tab);
-  else run_unit<KVT, D, false>(P, A, r, s, p, g, pg0, pg1, tab);
+  if (FUSE && c == nch - 1) run_unit<KVT, D, true>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf);
+  else run_unit<KVT, D, false>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf);
   if (nch == 1) {
     finish<KVT, D>(P, A, r, g);
     return;
