@@ -596,14 +596,18 @@ pkd_status decode_step(const pkd_layer* L, pkd_pool* pool, const pkd_rows* rows,
   // 1. qkv = W_qkv x  (norm: W_qkv carries the gain, outputs times 1/rms(x);
   //    rope: the q and k heads rotated by the row's position)
   const bool norm = (L->flags & PKD_LAYER_NORM) != 0, rope = (L->flags & PKD_LAYER_ROPE) != 0;
-  const bool need_cast = bf && !(tiled_family(L->w_qkv.family) && L->w_qkv.dtype == PKD_FP8_E4M3);
+  // the vector GEMV rounds x to bf16 as it loads it, so that a decode batch
+  // needs no pass of its own for the cast (the norm's pass writes the bf16 copy
+  // anyway)
+  const bool cast_in_gemv = bf && !norm && L->w_qkv.family == PKD_FAMILY_GEMV;
+  const bool need_cast = bf && !(tiled_family(L->w_qkv.family) && L->w_qkv.dtype == PKD_FP8_E4M3) && !cast_in_gemv;
   if (norm) {
     if ((s = rms_factor_launch(x, n, D, L->norm_eps, w.inv_x, need_cast ? w.x_in : nullptr, st, err))) return s;
   } else if (need_cast && (s = cast_bf16_launch(x, w.x_in, (int64_t)n * D, st, err))) {
     return s;
   }
   if (rope && (s = rope_table_launch(rows->pos, n, d, L->rope_base, w.cs, st, err))) return s;
-  auto in0 = proj_in(L->w_qkv, x, w.x_in);
+  const auto in0 = cast_in_gemv ? std::pair<const void*, int>{x, kXF32AsBf16} : proj_in(L->w_qkv, x, w.x_in);
   p = ProjArgs{};
   p.W = &L->w_qkv;
   p.x = in0.first;

@@ -124,6 +124,11 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
 inline bool tiled_family(int f) { return f == PKD_FAMILY_MFMA || f == PKD_FAMILY_MFMA_FP8; }
 
 // Projection launch used by gemv_rows and decode_step.
+// Projection input code used inside the library only (next to PKD_F32 and
+// PKD_BF16): f32 storage, each value rounded to bf16 (RNE) as the vector GEMV
+// loads it, which gives the same products as rounding it in a pass of its own.
+constexpr int32_t kXF32AsBf16 = 3;
+
 struct ProjArgs {
   const pkd_matrix* W;
   const void* x;

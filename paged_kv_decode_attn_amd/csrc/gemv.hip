@@ -74,10 +74,19 @@ __device__ __forceinline__ void decode_w(u32x4 v, float* w) {
   }
 }
 
-// Loads E activation values of row r at element k (f32 or bf16 storage).
+// Loads E activation values of row r at element k (XT 0: f32, 1: bf16, 3: f32
+// rounded to bf16 as loaded).
 template <int XT, int E>
 __device__ __forceinline__ void load_x(const uint8_t* x, int64_t stride, int r, int k, float* out) {
-  if constexpr (XT == 0) {
+  if constexpr (XT == 3) {
+    const float* p = reinterpret_cast<const float*>(x) + (int64_t)r * stride + k;
+#pragma unroll
+    for (int i = 0; i < E; i += 4) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + i);
+      const unsigned a = pack_bf16(v[0], v[1]), b = pack_bf16(v[2], v[3]);
+      out[i] = bf16lo(a); out[i + 1] = bf16hi(a); out[i + 2] = bf16lo(b); out[i + 3] = bf16hi(b);
+    }
+  } else if constexpr (XT == 0) {
     const float* p = reinterpret_cast<const float*>(x) + (int64_t)r * stride + k;
 #pragma unroll
     for (int i = 0; i < E; i += 4) {
@@ -194,14 +203,21 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
     for (int u = 0; u < U; ++u) {
       const int j = j0 + 64 * KS * u;
       if (j >= nvec) break;
-      if constexpr (WT == 1 && XT == 1) {
+      if constexpr (WT == 1 && (XT == 1 || XT == 3)) {
         // bf16 x bf16: the packed pairs go straight into the dot-2 instruction
         // (exact products, fp32 sums), pairs (0,1), (2,3), (4,5), (6,7) in order
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if (r0 + r >= P.n_rows) break;
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(P.x) +
-                                                           (int64_t)(r0 + r) * P.x_stride + 8 * j);
+          u32x4 xv;
+          if constexpr (XT == 1) {
+            xv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(P.x) +
+                                                 (int64_t)(r0 + r) * P.x_stride + 8 * j);
+          } else {
+            const float* xf = reinterpret_cast<const float*>(P.x) + (int64_t)(r0 + r) * P.x_stride + 8 * j;
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(xf), b = *reinterpret_cast<const f32x4_t*>(xf + 4);
+            xv = u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3])};
+          }
 #pragma unroll
           for (int i = 0; i < NR; ++i) {
             float a = acc[i][r];
@@ -499,6 +515,8 @@ template <int WT>
 static void launch_w(const GemvParams& P, int xt, bool silu, hipStream_t st) {
   if (xt == PKD_F32) {
     if (silu) launch_x<WT, 0, true>(P, st); else launch_x<WT, 0, false>(P, st);
+  } else if (xt == kXF32AsBf16) {
+    if (silu) launch_x<WT, 3, true>(P, st); else launch_x<WT, 3, false>(P, st);
   } else {
     if (silu) launch_x<WT, 1, true>(P, st); else launch_x<WT, 1, false>(P, st);
   }

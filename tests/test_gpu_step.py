@@ -76,6 +76,52 @@ def test_06b_b1(H, orc):
     check(H, y, want["y"], BAR_BF16, "0.6b-b1 y")
 
 
+def _step_from_public_calls(H, w, layer, pool):
+    """The step composed from the public calls, x rounded to bf16 by torch (RNE)
+    before the QKV projection: the path decode_step takes when the projection
+    family cannot round x itself."""
+    import paged_kv_decode_attn_amd as pkd
+    L = layer.layer
+    n, D, nq, nkv, d, F = w.n_rows, w.hidden, w.n_q, w.n_kv, w.head_dim, w.ffn
+    x = w.x.cuda().contiguous()
+    bf = torch.int16
+    xb = x.to(torch.bfloat16).view(bf).contiguous()
+    ws = lambda M: H.aligned_empty(max(pkd.pkd_gemv_workspace_bytes(M, n), 1))
+    qkv = torch.empty((n, (nq + 2 * nkv) * d), dtype=bf, device="cuda")
+    pkd.gemv_rows(L.w_qkv, xb, wl.BF16, n, qkv, wl.BF16, ws=ws(L.w_qkv))
+    q3 = qkv.view(n, nq + 2 * nkv, d)
+    q, k, v = (q3[:, :nq].contiguous(), q3[:, nq:nq + nkv].contiguous(), q3[:, nq + nkv:].contiguous())
+    s, p = H.rows_tensors(w.seq, w.pos)
+    rows = pkd.make_rows(s, p, len(set(w.seq.tolist())) == n)
+    att = torch.empty((n, nq * d), dtype=bf, device="cuda")
+    pkd.paged_attn_decode(pool.handle, rows, nq, q, k, v, att, wl.BF16,
+                          H.aligned_empty(max(pkd.pkd_attn_workspace_bytes(pool.handle, nq, n), 1)))
+    h = torch.empty((n, D), dtype=torch.float32, device="cuda")
+    hb = torch.empty((n, D), dtype=bf, device="cuda")
+    pkd.gemv_rows(L.w_o, att, wl.BF16, n, h, wl.F32, residual=x, y_bf16=hb, ws=ws(L.w_o))
+    a = torch.empty((n, F), dtype=bf, device="cuda")
+    pkd.gemv_rows(L.w_gate_up, hb, wl.BF16, n, a, wl.BF16, silu_pair=True, ws=ws(L.w_gate_up))
+    y = torch.empty((n, D), dtype=torch.float32, device="cuda")
+    pkd.gemv_rows(L.w_down, a, wl.BF16, n, y, wl.F32, residual=h, ws=ws(L.w_down))
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("0.6b-b1-bf16", dict()),
+    ("0.6b-mixed-bf16", dict(n_decode=20, chunk_rows=6, chunk=4, long_max=1200, family=wl.GEMV)),
+])
+def test_step_vector_family_rounds_x_in_load(H, name, kw):
+    """With the vector GEMV family, decode_step rounds x to bf16 inside the QKV
+    projection instead of in a pass of its own; the step's bits equal those of
+    the public calls fed x rounded by torch."""
+    w = wl.make(name, "cpu", **kw)
+    layer = H.GpuLayer(w)
+    y_step = layer.step(H.GpuPool(w), w.seq, w.pos, w.x)
+    y_calls = _step_from_public_calls(H, w, layer, H.GpuPool(w))
+    assert torch.equal(y_step, y_calls)
+
+
 def test_06b_b1_mfma_family(H, orc):
     w = wl.make("0.6b-b1-bf16", "cpu", family=wl.MFMA)
     pool = H.GpuPool(w)
