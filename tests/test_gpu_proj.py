@@ -164,16 +164,19 @@ def test_mfma_parity(H, orc, fam, wdt, xdt, rows, cols, n, silu, res, out, S):
     assert H.rel_err(H.values(yb, wl.BF16)[idx], want) <= TOL_BF16
 
 
-def test_mfma_tile_height_invariance(H):
-    """A large batch runs on the 256-row activation tile and a small one on the
-    128-row tile; a row's outputs are bit-identical either way."""
-    rows, cols = 16384, 512
+@pytest.mark.parametrize("k_splits", [1, 2])
+def test_mfma_tile_height_invariance(H, k_splits):
+    """A large batch runs on the 256-row activation tile (2,048 rows over 64
+    weight tiles: two rounds of 256-row tiles against four of 128-row ones) and
+    a small one on the 128-row tile; a row's outputs are bit-identical either
+    way, with and without a K split."""
+    rows, cols, n_all = 16384, 512, 2048
     W, s = make_w(rows, cols, wl.BF16, 11)
-    x = make_x(1100, cols, wl.BF16, 12)
-    full, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, 1, x, wl.BF16, 1100, wl.F32)
+    x = make_x(n_all, cols, wl.BF16, 12)
+    full, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, 1, x, wl.BF16, n_all, wl.F32, k_splits=k_splits)
     full = full.cpu()
-    for r, n in [(0, 3), (255, 2), (1097, 3), (600, 40)]:
-        part, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, 1, x[r:r + n], wl.BF16, n, wl.F32)
+    for r, n in [(0, 3), (255, 2), (2045, 3), (600, 40), (1100, 129)]:
+        part, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, 1, x[r:r + n], wl.BF16, n, wl.F32, k_splits=k_splits)
         assert torch.equal(part.cpu(), full[r:r + n]), (r, n)
 
 
