@@ -907,21 +907,36 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) o[j] = 0.f;
   if (nch > 0) {
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < nch; c0 += kWave)
+    // lane c holds (m, l) of chunk c; chunks past the first 64 are read again
+    // below, once the maximum is known
+    float m0 = -INFINITY, l0 = 0.f;
+    if (l < nch) {
+      const int64_t rec = rec_of(P, r, l, g, n);
+      m0 = P.part_ml[2 * rec];
+      l0 = P.part_ml[2 * rec + 1];
+    }
+    float M = m0;
+    for (int c0 = kWave; c0 < nch; c0 += kWave)
       if (c0 + l < nch) M = fmaxf(M, P.part_ml[2 * rec_of(P, r, c0 + l, g, n)]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
     float L = 0.f;
     for (int c0 = 0; c0 < nch; c0 += kWave) {
       float wl = 0.f, ll = 0.f;
-      if (c0 + l < nch) {
+      if (c0 == 0) {
+        if (l < nch) {
+          wl = fast_exp2(m0 - M);
+          ll = l0;
+        }
+      } else if (c0 + l < nch) {
         const int64_t rec = rec_of(P, r, c0 + l, g, n);
         wl = fast_exp2(P.part_ml[2 * rec] - M);
         ll = P.part_ml[2 * rec + 1];
       }
       const int cn = min(kWave, nch - c0);
-      constexpr int U = 4;
+      // sixteen chunk records requested at a time (one round trip for up to
+      // sixteen chunks), then added in chunk order
+      constexpr int U = 16;
       for (int c = 0; c < cn; c += U) {
         float v[U][PER];
 #pragma unroll
@@ -930,13 +945,20 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
 #pragma unroll
           for (int j = 0; j < PER; ++j) v[u][j] = P.part_o[rec * D + PER * l + j];
         }
+        // no branch between the loads and the sums (a break here let the
+        // compiler wait for each record in turn); records past cn are selected
+        // away, so every bit is that of adding chunks c .. cn - 1 in order
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          if (c + u >= cn) break;
-          const float w = __shfl(wl, c + u, kWave);
-          L += __shfl(ll, c + u, kWave) * w;
+          const bool in = c + u < cn;
+          const float w = __shfl(wl, min(c + u, cn - 1), kWave);
+          const float Ln = L + __shfl(ll, min(c + u, cn - 1), kWave) * w;
+          L = in ? Ln : L;
 #pragma unroll
-          for (int j = 0; j < PER; ++j) o[j] += v[u][j] * w;
+          for (int j = 0; j < PER; ++j) {
+            const float on = o[j] + v[u][j] * w;
+            o[j] = in ? on : o[j];
+          }
         }
       }
     }
