@@ -543,25 +543,64 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams P) {
 
 // Per-row fp8 quantisation of a projection input: s = max|x| / 448 (fp32
 // division; 1 for an all-zero row), codes = E4M3 RNE(x / s), saturating.
+// Each thread takes groups of 8 consecutive elements (K is a multiple of 64),
+// four groups in flight: a group index past the row is clamped to its last
+// group, whose values the maximum already holds and whose codes another
+// thread writes with the same bytes, so no load or store is conditional (a
+// condition between the loads and their use let the compiler wait for each
+// load in turn).
+template <int XT>
+__device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8]) {
+  if constexpr (XT == 0) {
+    const float* p = reinterpret_cast<const float*>(x) + off;
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p), b = *reinterpret_cast<const f32x4_t*>(p + 4);
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3]; v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
+    const unsigned d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16lo(d[j]);
+      v[2 * j + 1] = bf16hi(d[j]);
+    }
+  }
+}
+
 template <int XT>
 __global__ __launch_bounds__(256) void act_quant_kernel(const void* x, int K, uint8_t* codes, float* scales) {
   __shared__ float red[4];
   const int r = blockIdx.x, t = threadIdx.x;
-  auto val = [&](int k) -> float {
-    if constexpr (XT == 0) return reinterpret_cast<const float*>(x)[(int64_t)r * K + k];
-    else return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(x)[(int64_t)r * K + k]);
-  };
+  const int ng = K / 8;
+  constexpr int U = 4;
   float m = 0.f;
-  for (int k = t; k < K; k += 256) m = fmaxf(m, fabsf(val(k)));
+  for (int g0 = t; g0 < ng; g0 += 256 * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load8<XT>(x, (int64_t)r * K + 8 * min(g0 + 256 * u, ng - 1), v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
+  }
   m = wave_max(m);
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = m > 0.f ? m / 448.0f : 1.0f;
   if (t == 0) scales[r] = s;
-  for (int k = 2 * t; k < K; k += 512) {
-    const unsigned c = f32x2_to_fp8x2(val(k) / s, val(k + 1) / s);
-    *reinterpret_cast<uint16_t*>(codes + (int64_t)r * K + k) = (uint16_t)c;
+  for (int g0 = t; g0 < ng; g0 += 256 * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load8<XT>(x, (int64_t)r * K + 8 * min(g0 + 256 * u, ng - 1), v[u]);
+    __builtin_amdgcn_sched_barrier(0);  // all four loads issue before the divisions
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      unsigned c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = f32x2_to_fp8x2(v[u][2 * j] / s, v[u][2 * j + 1] / s);
+      *reinterpret_cast<u32x2*>(codes + (int64_t)r * K + 8 * min(g0 + 256 * u, ng - 1)) =
+          u32x2{c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
+    }
   }
 }
 
