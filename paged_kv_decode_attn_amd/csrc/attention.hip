@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pkd {
@@ -934,33 +936,38 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
         ll = P.part_ml[2 * rec + 1];
       }
       const int cn = min(kWave, nch - c0);
-      // sixteen chunk records requested at a time (one round trip for up to
-      // sixteen chunks), then added in chunk order
-      constexpr int U = 16;
-      for (int c = 0; c < cn; c += U) {
-        float v[U][PER];
+      // U chunk records requested at a time (one round trip for up to U
+      // chunks; 4 for short rows, so that the clamped extra requests stay
+      // few), then added in chunk order.  No branch between the loads and the
+      // sums (a break there let the compiler wait for each record in turn);
+      // records past cn are selected away, so every bit is that of adding
+      // chunks c .. cn - 1 in order.
+      auto accumulate = [&](auto u_const) {
+        constexpr int U = decltype(u_const)::value;
+        for (int c = 0; c < cn; c += U) {
+          float v[U][PER];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t rec = rec_of(P, r, c0 + min(c + u, cn - 1), g, n);
+          for (int u = 0; u < U; ++u) {
+            const int64_t rec = rec_of(P, r, c0 + min(c + u, cn - 1), g, n);
 #pragma unroll
-          for (int j = 0; j < PER; ++j) v[u][j] = P.part_o[rec * D + PER * l + j];
-        }
-        // no branch between the loads and the sums (a break here let the
-        // compiler wait for each record in turn); records past cn are selected
-        // away, so every bit is that of adding chunks c .. cn - 1 in order
+            for (int j = 0; j < PER; ++j) v[u][j] = P.part_o[rec * D + PER * l + j];
+          }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const bool in = c + u < cn;
-          const float w = __shfl(wl, min(c + u, cn - 1), kWave);
-          const float Ln = L + __shfl(ll, min(c + u, cn - 1), kWave) * w;
-          L = in ? Ln : L;
+          for (int u = 0; u < U; ++u) {
+            const bool in = c + u < cn;
+            const float w = __shfl(wl, min(c + u, cn - 1), kWave);
+            const float Ln = L + __shfl(ll, min(c + u, cn - 1), kWave) * w;
+            L = in ? Ln : L;
 #pragma unroll
-          for (int j = 0; j < PER; ++j) {
-            const float on = o[j] + v[u][j] * w;
-            o[j] = in ? on : o[j];
+            for (int j = 0; j < PER; ++j) {
+              const float on = o[j] + v[u][j] * w;
+              o[j] = in ? on : o[j];
+            }
           }
         }
-      }
+      };
+      if (cn <= 4) accumulate(std::integral_constant<int, 4>{});
+      else accumulate(std::integral_constant<int, 16>{});
     }
     const float inv = 1.0f / L;
 #pragma unroll
