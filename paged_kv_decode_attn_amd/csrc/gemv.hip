@@ -315,10 +315,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
   }
 }
 
-// Matrix-core products for bf16 activations with bf16 or fp8 weights.  One
-// wave takes 16 weight rows (SILU: 8 gate rows and their 8 up rows) and 16
-// activation rows (rows past the batch are zeros), one 16 x 16 x 32 product per
-// 32 k.  The weights go straight from HBM into registers: lane (i, g) =
+// Matrix-core products for bf16 activations with bf16 or fp8 weights.  A row
+// group is 16 weight rows (SILU: 8 gate rows and their 8 up rows); one wave
+// takes RB row groups and 16 activation rows (rows past the batch are zeros),
+// one 16 x 16 x 32 product per row group and 32 k, the RB products sharing the
+// activation operand.  The weights go straight from HBM into registers: lane (i, g) =
 // (l % 16, l / 16) holds 8 elements of weight row i at k = 32 t + 8 g, so one
 // wave load is 16 rows x 64 contiguous bytes (32 for fp8, widened exactly to
 // bf16 in registers); the activations are the other operand in the same
@@ -333,75 +334,94 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
 // batch 1.
 // GATHER: one activation row per block column (column 0 of the product), the
 // 16 weight rows taken from its candidate list; everything else as dense.
-template <int WT, bool SILU, int KS, bool GATHER>
+template <int WT, bool SILU, int KS, bool GATHER, int RB>
 __global__ __launch_bounds__(KS > 4 ? 64 * KS : 256) void gemv_mfma_kernel(GemvParams P) {
   static_assert(!(GATHER && SILU), "gathered rows: no silu pair");
+  static_assert(!GATHER || RB == 1, "gathered rows: one row group per wave");
   constexpr int NW = KS > 4 ? KS : 4;  // waves per block
-  constexpr int GPB = NW / KS;         // row groups per block
+  constexpr int GPB = NW / KS;         // wave row slots per block
   constexpr int NP = SILU ? 8 : 16;    // outputs per row group
   const int wib = threadIdx.x >> 6, l = lane_id(), i = l & 15, g = l >> 4;
   const int kw = wib % KS;
-  const int o0 = (blockIdx.x * GPB + wib / KS) * NP;
+  const int o0 = (blockIdx.x * GPB + wib / KS) * NP * RB;  // first output of row group 0 of this wave
   int n_out = P.n_out;
   if constexpr (GATHER) n_out = min(max(P.n_cand[blockIdx.y], 0), P.max_cand);
   if (o0 >= n_out) return;  // uniform over the block when KS > 1
-  // weight row of lane i (rows past the end repeat the last one; not stored)
-  int wr;
+  // weight row of lane i in row group b (rows past the end repeat the last one; not stored)
+  int wr[RB];
   bool bad = false;
-  if constexpr (GATHER) {
-    const int j = P.cand[(int64_t)blockIdx.y * P.max_cand + min(o0 + i, n_out - 1)];
-    bad = j < 0 || j >= P.rows;
-    wr = bad ? 0 : j;
-  } else if constexpr (SILU) {
-    wr = i < 8 ? min(o0 + i, P.n_out - 1) : P.n_out + min(o0 + i - 8, P.n_out - 1);
-  } else {
-    wr = min(o0 + i, P.rows - 1);
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int ob = o0 + b * NP;
+    if constexpr (GATHER) {
+      const int j = P.cand[(int64_t)blockIdx.y * P.max_cand + min(ob + i, n_out - 1)];
+      bad = j < 0 || j >= P.rows;
+      wr[b] = bad ? 0 : j;
+    } else if constexpr (SILU) {
+      wr[b] = i < 8 ? min(ob + i, P.n_out - 1) : P.n_out + min(ob + i - 8, P.n_out - 1);
+    } else {
+      wr[b] = min(ob + i, P.rows - 1);
+    }
   }
   // activation row of lane i (the product's column i)
   const int xr = GATHER ? (i == 0 ? (int)blockIdx.y : -1) : (blockIdx.y * 16 + i < P.n_rows ? blockIdx.y * 16 + i : -1);
   constexpr int WB = WT == 1 ? 16 : 8;  // weight bytes per lane and k-step
-  const uint8_t* wp = P.W + (int64_t)wr * P.cols * (WT == 1 ? 2 : 1) + WB * g;
+  const uint8_t* wp[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) wp[b] = P.W + (int64_t)wr[b] * P.cols * (WT == 1 ? 2 : 1) + WB * g;
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(P.x) + (int64_t)(xr < 0 ? 0 : xr) * P.x_stride + 8 * g;
   const int nst = P.cols / 32;
   const int t0 = nst * kw / KS, t1 = nst * (kw + 1) / KS;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   constexpr int U = 8;
   for (int t = t0; t < t1; t += U) {
-    u32x4 wv[U], xv[U];
+    u32x4 wv[U][RB], xv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + u >= t1) break;
-      if constexpr (WT == 1) {
-        wv[u] = *reinterpret_cast<const u32x4*>(wp + 64 * (int64_t)(t + u));
-      } else {
-        const u32x2 c = *reinterpret_cast<const u32x2*>(wp + 32 * (int64_t)(t + u));
-        wv[u] = u32x4{c.x, c.y, 0u, 0u};
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        if constexpr (WT == 1) {
+          wv[u][b] = *reinterpret_cast<const u32x4*>(wp[b] + 64 * (int64_t)(t + u));
+        } else {
+          const u32x2 c = *reinterpret_cast<const u32x2*>(wp[b] + 32 * (int64_t)(t + u));
+          wv[u][b] = u32x4{c.x, c.y, 0u, 0u};
+        }
       }
       xv[u] = xr >= 0 ? *reinterpret_cast<const u32x4*>(xp + 32 * (int64_t)(t + u)) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + u >= t1) break;
-      u32x4 a = wv[u];
-      if constexpr (WT == 2) {
-        const u32x2 lo = fp8x4_to_bf16x4(wv[u].x), hi = fp8x4_to_bf16x4(wv[u].y);
-        a = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        u32x4 a = wv[u][b];
+        if constexpr (WT == 2) {
+          const u32x2 lo = fp8x4_to_bf16x4(wv[u][b].x), hi = fp8x4_to_bf16x4(wv[u][b].y);
+          a = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                         __builtin_bit_cast(bf16x8_t, xv[u]), acc[b], 0, 0, 0);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, xv[u]),
-                                                    acc, 0, 0, 0);
     }
   }
   if constexpr (KS > 1) {
-    __shared__ f32x4_t part[KS][64];
-    part[kw][l] = acc;
+    __shared__ f32x4_t part[KS][RB][64];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) part[kw][b][l] = acc[b];
     __syncthreads();
     if (kw != 0) return;
-    f32x4_t tsum = part[0][l];
 #pragma unroll
-    for (int w = 1; w < KS; ++w) tsum += part[w][l];
-    acc = tsum;
+    for (int b = 0; b < RB; ++b) {
+      f32x4_t tsum = part[0][b][l];
+#pragma unroll
+      for (int w = 1; w < KS; ++w) tsum += part[w][b][l];
+      acc[b] = tsum;
+    }
   }
-  // lane (rg, col) holds outputs o0 + 4 rg + v (v < 4) of activation column col
+  // lane (rg, col) holds outputs o0 + NP b + 4 rg + v (v < 4) of activation column col
   const int col = l & 15, rg = l >> 4;
   if constexpr (GATHER) {
     bool bv[4];
@@ -412,54 +432,54 @@ __global__ __launch_bounds__(KS > 4 ? 64 * KS : 256) void gemv_mfma_kernel(GemvP
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int o = o0 + 4 * rg + v;
-      if (o < n_out) y[o] = bv[v] ? __builtin_nanf("") : acc[v] * P.w_scale;
+      if (o < n_out) y[o] = bv[v] ? __builtin_nanf("") : acc[0][v] * P.w_scale;
     }
     return;
   }
-  float vo[4];
-  int ob;  // first output of this lane
-  if constexpr (SILU) {
-    float up[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) up[v] = shfl_xor(acc[v], 32);
-    if (rg >= 2) return;
-    const int r = blockIdx.y * 16 + col;
-    if (r >= P.n_rows) return;
-    const float rsc = P.row_scale ? P.row_scale[r] : 1.0f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float gt = acc[v] * P.w_scale, u = up[v] * P.w_scale;
-      if (P.row_scale) { gt *= rsc; u *= rsc; }
-      vo[v] = silu(gt) * u;
-    }
-    ob = o0 + 4 * rg;
-  } else {
-    const int r = blockIdx.y * 16 + col;
-    if (r >= P.n_rows) return;
-    const float rsc = P.row_scale ? P.row_scale[r] : 1.0f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      vo[v] = acc[v] * P.w_scale;
-      if (P.row_scale) vo[v] *= rsc;
-    }
-    ob = o0 + 4 * rg;
-    if (P.rope_cs && ob < P.rope_cols) {
-      rope_pair(P.rope_cs, P.rope_hd, r, ob, vo[0], vo[1]);
-      rope_pair(P.rope_cs, P.rope_hd, r, ob + 2, vo[2], vo[3]);
-    }
-  }
   const int r = blockIdx.y * 16 + col;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int o = ob + v;
-    if (o >= P.n_out) break;
-    float val = vo[v];
-    if constexpr (!SILU) {
-      if (P.residual) val += P.residual[(int64_t)r * P.n_out + o];
+  for (int b = 0; b < RB; ++b) {
+    float vo[4];
+    int ob;  // first output of this lane in row group b
+    if constexpr (SILU) {
+      float up[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) up[v] = shfl_xor(acc[b][v], 32);
+      if (rg >= 2 || r >= P.n_rows) continue;
+      const float rsc = P.row_scale ? P.row_scale[r] : 1.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float gt = acc[b][v] * P.w_scale, u = up[v] * P.w_scale;
+        if (P.row_scale) { gt *= rsc; u *= rsc; }
+        vo[v] = silu(gt) * u;
+      }
+      ob = o0 + NP * b + 4 * rg;
+    } else {
+      if (r >= P.n_rows) continue;
+      const float rsc = P.row_scale ? P.row_scale[r] : 1.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        vo[v] = acc[b][v] * P.w_scale;
+        if (P.row_scale) vo[v] *= rsc;
+      }
+      ob = o0 + NP * b + 4 * rg;
+      if (P.rope_cs && ob < P.rope_cols) {
+        rope_pair(P.rope_cs, P.rope_hd, r, ob, vo[0], vo[1]);
+        rope_pair(P.rope_cs, P.rope_hd, r, ob + 2, vo[2], vo[3]);
+      }
     }
-    if (P.y_bf16) reinterpret_cast<uint16_t*>(P.y)[(int64_t)r * P.y_stride + o] = (uint16_t)f32_to_bf16_bits(val);
-    else reinterpret_cast<float*>(P.y)[(int64_t)r * P.y_stride + o] = val;
-    if (P.y2) P.y2[(int64_t)r * P.n_out + o] = (uint16_t)f32_to_bf16_bits(val);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int o = ob + v;
+      if (o >= P.n_out) break;
+      float val = vo[v];
+      if constexpr (!SILU) {
+        if (P.residual) val += P.residual[(int64_t)r * P.n_out + o];
+      }
+      if (P.y_bf16) reinterpret_cast<uint16_t*>(P.y)[(int64_t)r * P.y_stride + o] = (uint16_t)f32_to_bf16_bits(val);
+      else reinterpret_cast<float*>(P.y)[(int64_t)r * P.y_stride + o] = val;
+      if (P.y2) P.y2[(int64_t)r * P.n_out + o] = (uint16_t)f32_to_bf16_bits(val);
+    }
   }
 }
 
@@ -475,12 +495,15 @@ static void launch_mfma(const GemvParams& P, int tiles_y, hipStream_t st) {
   constexpr int NP = SILU ? 8 : 16;
   const int groups = ((GATHER ? P.max_cand : P.n_out) + NP - 1) / NP;
   const int ks = gemv_mfma_k_split(P.rows);
+  // Dense matrices with 1,024 or more row groups give each wave two row
+  // groups, which share its activation loads.
+  constexpr int RB = GATHER ? 1 : 2;
   if (ks == 8)
-    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 8, GATHER>), dim3(groups, tiles_y), dim3(512), 0, st, P);
+    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 8, GATHER, 1>), dim3(groups, tiles_y), dim3(512), 0, st, P);
   else if (ks == 4)
-    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 4, GATHER>), dim3(groups, tiles_y), dim3(256), 0, st, P);
+    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 4, GATHER, RB>), dim3((groups + RB - 1) / RB, tiles_y), dim3(256), 0, st, P);
   else
-    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 1, GATHER>), dim3((groups + 3) / 4, tiles_y), dim3(256), 0, st, P);
+    hipLaunchKernelGGL((gemv_mfma_kernel<WT, SILU, 1, GATHER, RB>), dim3((groups + 4 * RB - 1) / (4 * RB), tiles_y), dim3(256), 0, st, P);
 }
 
 // K split of a matrix: 4 when its row groups alone would give fewer than
