@@ -96,6 +96,9 @@ GEMV_FAMILY_CASES = [(0,) + c for c in GEMV_CASES] + [
     (3,) + c for c in GEMV_CASES if c[1] == wl.BF16 and c[0] != wl.F32] + [
     (3, wl.BF16, wl.BF16, 1000, 3584, 37, False, True, wl.F32),  # three 16-row activation tiles, ragged
     (3, wl.FP8, wl.BF16, 2 * 520, 1024, 20, True, False, wl.BF16),
+    # 4,096+ row groups: one wave per K range, two row groups per wave (odd count)
+    (3, wl.BF16, wl.BF16, 70000, 256, 17, False, True, wl.F32),
+    (3, wl.FP8, wl.BF16, 2 * 33000, 256, 9, True, False, wl.BF16),
 ]
 
 
