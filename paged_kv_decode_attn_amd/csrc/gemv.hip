@@ -319,16 +319,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams P) {
 // group is 16 weight rows (SILU: 8 gate rows and their 8 up rows); one wave
 // takes RB row groups and 16 activation rows (rows past the batch are zeros),
 // one 16 x 16 x 32 product per row group and 32 k, the RB products sharing the
-// activation operand.  The weights go straight from HBM into registers: lane (i, g) =
-// (l % 16, l / 16) holds 8 elements of weight row i at k = 32 t + 8 g, so one
-// wave load is 16 rows x 64 contiguous bytes (32 for fp8, widened exactly to
-// bf16 in registers); the activations are the other operand in the same
-// layout.  KS waves of a block (KS > 1: one row group per block) split the
-// k-steps into contiguous ranges and add their partial sums through LDS in
-// the order 0 .. KS - 1.  A product's column depends only on its own
-// activation row and the split only on the matrix shape, so a row's result
-// never depends on the batch.  This is the PKD_FAMILY_GEMV_MFMA family: the
-// matrix cores keep it near the weight stream up to 16 activation rows per
+// activation operand.  The weights go straight from HBM into registers: lane
+// (i, g) = (l % 16, l / 16) holds 8 elements of weight row i at k = 32 t + 8 g,
+// so one wave load is 16 rows x 64 contiguous bytes (32 for fp8, widened
+// exactly to bf16 in registers); the activations are the other operand in the
+// same layout.  KS waves of a block (KS > 1: the block holds one wave's row
+// groups) split the k-steps into contiguous ranges and add their partial sums
+// through LDS in the order 0 .. KS - 1.  A product's column depends only on
+// its own activation row and the split only on the matrix shape, so a row's
+// result never depends on the batch.  This is the PKD_FAMILY_GEMV_MFMA family:
+// the matrix cores keep it near the weight stream up to 16 activation rows per
 // pass, where the vector-ALU form is bound by its multiply-adds from about 8,
 // but its 64-byte weight runs stream below the vector form's 1 KiB runs at
 // batch 1.
