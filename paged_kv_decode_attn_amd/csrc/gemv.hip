@@ -375,7 +375,8 @@ __global__ __launch_bounds__(KS > 4 ? 64 * KS : 256) void gemv_mfma_kernel(GemvP
   f32x4_t acc[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 8;
+  // k-steps in flight per wave: 6 with two row groups keeps 104 VGPRs, four waves per SIMD
+  constexpr int U = RB > 1 ? 6 : 8;
   for (int t = t0; t < t1; t += U) {
     u32x4 wv[U][RB], xv[U];
 #pragma unroll
