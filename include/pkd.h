@@ -83,12 +83,13 @@ typedef enum {
                              matrix-core rate, but each instruction sums its 128 products with
                              ~17 significant bits (measured relative error of a projection
                              ~2e-5 instead of ~1e-7) */
-  PKD_FAMILY_GEMV_MFMA = 3 /* GEMV on the matrix cores for decode batches of about 8 to 16: one
-                             wave per 16 weight rows read straight into registers, the batch as
-                             the product's 16 columns; bf16 or fp8 weights (fp8 decoded exactly),
-                             bf16 activations, fp32 accumulation.  Measured on the 7B matrices:
-                             faster than PKD_FAMILY_GEMV from batch 8 (156 against 199 us at
-                             16), slower below (103 against 93 us at 1). */
+  PKD_FAMILY_GEMV_MFMA = 3 /* GEMV on the matrix cores for decode batches of about 8 to 16:
+                             groups of 16 weight rows read straight into registers (one or two
+                             groups per wave, by matrix height), the batch as the product's 16
+                             columns; bf16 or fp8 weights (fp8 decoded exactly), bf16
+                             activations, fp32 accumulation.  Measured on the 7B matrices:
+                             faster than PKD_FAMILY_GEMV from batch 8 (146 against 200 us at
+                             16), slower below (106 against 94 us at 1). */
 } pkd_family;
 
 /* ------------------------------------------------------------------------ */
