@@ -496,6 +496,9 @@ enum { ORC_NORM = 1, ORC_ROPE = 2 };
 
 typedef struct {
   double *qkv, *attn, *h, *a, *y; /* [n][...] outputs, any may be NULL */
+  /* the stored stages before their rounding to the activation dtype: the
+   * exact value of each stage given the stored values of the one before */
+  double *qkv_raw, *attn_raw, *a_raw;
 } orc_outputs;
 
 /* Projection of n input rows Z [n][cols] by W: the input is first taken in
@@ -559,6 +562,7 @@ int orc_decode_step(const orc_layer* L, const orc_history* H, int n, const int32
     }
     if (L->flags & ORC_ROPE) orc_rope(row, nq + nkv, d, pos[r], L->rope_base);
   }
+  if (out && out->qkv_raw) memcpy(out->qkv_raw, qkv, sizeof(double) * n * nqkv);
   for (int64_t i = 0; i < (int64_t)n * nqkv; ++i) qkv[i] = round_act(qkv[i], L->act_dtype);
   for (int r = 0; r < n; ++r) {
     const double* row = qkv + (int64_t)r * nqkv;
@@ -571,6 +575,7 @@ int orc_decode_step(const orc_layer* L, const orc_history* H, int n, const int32
   /* append every row, then attend every row */
   orc_attn_geom G = {nq, nkv, d, L->kv_dtype, L->k_scale, L->v_scale};
   if (attention_core(&G, H, n, seq, pos, qv, kv, vv, att)) goto done;
+  if (out && out->attn_raw) memcpy(out->attn_raw, att, sizeof(double) * n * nq * d);
   for (int64_t i = 0; i < (int64_t)n * nq * d; ++i) att[i] = round_act(att[i], L->act_dtype);
   if (out && out->attn) memcpy(out->attn, att, sizeof(double) * n * nq * d);
 
@@ -590,7 +595,9 @@ int orc_decode_step(const orc_layer* L, const orc_history* H, int n, const int32
       double f = (L->flags & ORC_NORM) ? orc_inv_rms(h + (int64_t)r * D, D, L->norm_eps) : 1.0;
       for (int j = 0; j < F; ++j) {
         double g = gu[(int64_t)r * 2 * F + j] * f, u = gu[(int64_t)r * 2 * F + F + j] * f;
-        a[(int64_t)r * F + j] = round_act(g / (1.0 + exp(-g)) * u, L->act_dtype);
+        double v = g / (1.0 + exp(-g)) * u;
+        if (out && out->a_raw) out->a_raw[(int64_t)r * F + j] = v;
+        a[(int64_t)r * F + j] = round_act(v, L->act_dtype);
       }
     }
     if (out && out->a) memcpy(out->a, a, sizeof(double) * n * F);

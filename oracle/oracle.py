@@ -209,7 +209,8 @@ class _Layer(ctypes.Structure):
 
 class _Out(ctypes.Structure):
     _fields_ = [("qkv", ctypes.c_void_p), ("attn", ctypes.c_void_p), ("h", ctypes.c_void_p),
-                ("a", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+                ("a", ctypes.c_void_p), ("y", ctypes.c_void_p), ("qkv_raw", ctypes.c_void_p),
+                ("attn_raw", ctypes.c_void_p), ("a_raw", ctypes.c_void_p)]
 
 
 class History:
@@ -269,11 +270,12 @@ def gather_history(pages: np.ndarray, n_kv: int, d: int, kv_dtype: int, table_ro
     return k, v
 
 
-def decode_step(layer: dict, hist: History, seq, pos, x) -> dict:
+def decode_step(layer: dict, hist: History, seq, pos, x, raw: bool = False) -> dict:
     """layer: hidden, n_q, n_kv, head_dim, ffn, w_dtype, w_qkv, w_o, w_gu, w_d (code
     arrays), s_qkv, s_o, s_gu, s_d, act_dtype, act_fp8, kv_dtype, k_scale, v_scale;
     optional norm (bool, gains already folded into w_qkv / w_gu), norm_eps,
-    rope (bool), rope_base."""
+    rope (bool), rope_base.  raw: also return qkv_raw, attn_raw, a_raw, the
+    stored stages before their rounding to the activation dtype."""
     seq = _c(seq, np.int32)
     pos = _c(pos, np.int32)
     x = _c(x, np.float32)
@@ -293,8 +295,14 @@ def decode_step(layer: dict, hist: History, seq, pos, x) -> dict:
             "h": np.empty((n, D)), "y": np.empty((n, D))}
     if F > 0:
         outs["a"] = np.empty((n, F))
+    if raw:  # each stored stage also before its rounding to the activation dtype
+        outs["qkv_raw"] = np.empty_like(outs["qkv"])
+        outs["attn_raw"] = np.empty_like(outs["attn"])
+        if F > 0:
+            outs["a_raw"] = np.empty_like(outs["a"])
     o = _Out(_ptr(outs["qkv"]), _ptr(outs["attn"]), _ptr(outs["h"]), _ptr(outs.get("a")),
-             _ptr(outs["y"]))
+             _ptr(outs["y"]), _ptr(outs.get("qkv_raw")), _ptr(outs.get("attn_raw")),
+             _ptr(outs.get("a_raw")))
     h = hist.struct()
     rc = lib().orc_decode_step(ctypes.byref(L), ctypes.byref(h), n, _ptr(seq), _ptr(pos), _ptr(x),
                                ctypes.byref(o))

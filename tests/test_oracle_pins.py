@@ -617,6 +617,73 @@ def test_step_fp8_tier_projection(orc):
         assert np.allclose(got, want, rtol=2 ** -7, atol=1e-6)
 
 
+def test_step_fp8_tier_composition(orc):
+    """fp8 tier, every stage, against torch fp64 library ops on decoded codes.
+    Each projection input is quantised per row: s = fp32(max|z|) / 448 (fp32
+    division), codes = torch's E4M3 conversion of z / s (fp32 division,
+    clamped to +-448 first), and the projection is s * s_W * (codes @ W8^T).
+    The quantised z is the f32 residual-stream value for x and h, and the
+    stored bf16 value for attn and a.  The row's key and value are appended
+    as E4M3 of (stored bf16 value) / scale in fp32; attention is torch's SDPA
+    over decoded K, V times their scales.  Stored outputs (qkv, attn, a) are
+    bf16; h and y stay in fp64.  Each stage starts from the oracle's stored
+    values of the previous one, so a rounding flip cannot cascade."""
+    rng = np.random.default_rng(27)
+    layer, hist, seq, pos, x = _small_layer(orc, rng, w_dtype=2, kv_dtype=2, act_fp8=1)
+    D, nq, nkv, d, F = (layer[k] for k in ("hidden", "n_q", "n_kv", "head_dim", "ffn"))
+    out = orc.decode_step(layer, hist, seq, pos, x)
+    e4 = torch.float8_e4m3fn
+
+    def bf(t):
+        return t.to(torch.bfloat16).double()
+
+    def W8(name, sname):
+        return torch.from_numpy(layer[name].copy()).view(e4).double() * float(layer[sname])
+
+    def proj(z32, name, sname):
+        z32 = z32.float()
+        s = z32.abs().amax(1, keepdim=True) / torch.tensor(448.0, dtype=torch.float32)
+        s = torch.where(s > 0, s, torch.ones_like(s))
+        codes = (z32 / s).clamp(-448.0, 448.0).to(e4).double()
+        return s.double() * (codes @ W8(name, sname).T)
+
+    def stored_bf16(a):  # oracle's stored bf16 values are exact in f32
+        return torch.from_numpy(a).float()
+    X = torch.from_numpy(x).float()
+    qkv = bf(proj(X, "w_qkv", "s_qkv"))
+    assert np.allclose(out["qkv"], qkv.numpy(), rtol=2 ** -7, atol=1e-6)
+    qkv = torch.from_numpy(out["qkv"])
+    ks, vs = float(layer["k_scale"]), float(layer["v_scale"])
+
+    def append(vals, sc):  # E4M3 of value / scale in fp32, decoded times the scale
+        return (vals.float() / torch.tensor(sc, dtype=torch.float32)).clamp(-448.0, 448.0).to(e4).double() * sc
+    att = []
+    for r in range(len(seq)):
+        o, L = hist.hist_off[r], hist.hist_len[r]
+        Kh = torch.from_numpy(hist.k[o:o + L].copy()).view(e4).double() * ks
+        Vh = torch.from_numpy(hist.v[o:o + L].copy()).view(e4).double() * vs
+        kn = append(qkv[r, nq * d:(nq + nkv) * d].reshape(1, nkv, d), ks)
+        vn = append(qkv[r, (nq + nkv) * d:].reshape(1, nkv, d), vs)
+        K = torch.cat([Kh, kn]).permute(1, 0, 2).repeat_interleave(nq // nkv, 0)
+        V = torch.cat([Vh, vn]).permute(1, 0, 2).repeat_interleave(nq // nkv, 0)
+        qh = qkv[r, :nq * d].reshape(nq, 1, d)
+        att.append(torch.nn.functional.scaled_dot_product_attention(qh, K, V)[:, 0].reshape(-1))
+    att = bf(torch.stack(att))
+    assert np.allclose(out["attn"], att.numpy(), rtol=2 ** -7, atol=1e-6)
+    h = X.double() + proj(stored_bf16(out["attn"]), "w_o", "s_o")
+    assert np.allclose(out["h"], h.numpy(), rtol=1e-10, atol=1e-12)
+    gu = proj(torch.from_numpy(out["h"]).float(), "w_gu", "s_gu")
+    a = bf(torch.nn.functional.silu(gu[:, :F]) * gu[:, F:])
+    assert np.allclose(out["a"], a.numpy(), rtol=2 ** -7, atol=1e-7)
+    y = torch.from_numpy(out["h"]) + proj(stored_bf16(out["a"]), "w_d", "s_d")
+    assert np.allclose(out["y"], y.numpy(), rtol=1e-10, atol=1e-12)
+    # the per-row scale matters: one scale over the whole batch gives other h
+    z = stored_bf16(out["attn"])
+    s_all = z.abs().amax() / torch.tensor(448.0, dtype=torch.float32)
+    h_tensor = X.double() + s_all.double() * ((z / s_all).clamp(-448, 448).to(e4).double() @ W8("w_o", "s_o").T)
+    assert not np.allclose(out["h"], h_tensor.numpy(), rtol=1e-10, atol=1e-12)
+
+
 @pytest.mark.parametrize("norm_rope", [False, True])
 def test_step_rows_independent_and_sequential(orc, norm_rope):
     """Rows are independent (any order, alone) and several rows of one sequence
