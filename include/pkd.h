@@ -18,19 +18,24 @@
  *    allocating).
  *  - Every call that launches work takes a stream (a hipStream_t passed as
  *    pkd_stream; NULL is the default stream), enqueues asynchronously and
- *    never synchronises the host, except block_table_set and pkd_pool_check,
- *    which say so.  No hot call allocates ([LRS] section 4, lesson 1: one
- *    workspace per request instead of allocation inside the decode loop).
+ *    never synchronises the host, except the admission-time pool calls
+ *    kv_pool_create, block_table_set and pkd_pool_check, which say so.  No
+ *    hot call allocates ([LRS] section 4, lesson 1: one workspace per request
+ *    instead of allocation inside the decode loop).
  *  - Every call returns a pkd_status (0 = PKD_OK).  If `err` is non-NULL it
  *    receives a typed refusal with the numbers involved ([GIE] "Batching
  *    without running out of cache": admission refuses with a typed reason and
  *    the numbers).  Host-visible arguments are validated before anything is
  *    launched; on refusal nothing is launched and nothing is modified.
  *  - Device pointers must be 16-byte aligned unless a call states otherwise.
- *  - Threads: calls on different pools, or calls that only read a pool
- *    (attention, decode_step, pkd_pool_info_get), may run from several host
- *    threads at once.  block_table_set and kv_pool_destroy change a pool's
- *    host state and must not overlap any other call on the same pool.
+ *  - Threads and streams: paged_attn_decode and decode_step write the pool
+ *    (each row's own key and value, and the sticky error word).  Calls on
+ *    different pools may run from several host threads and streams at once;
+ *    calls on one pool may overlap only when they touch disjoint sequences
+ *    (and no shared page is appended to).  block_table_set and
+ *    kv_pool_destroy change a pool's host state and must not overlap any
+ *    other call on the same pool; launches that read the tables a
+ *    block_table_set replaces must be complete before it is called.
  *  - Determinism: the output of a row depends only on that row's inputs, its
  *    sequence's pages, the weights and the fixed configuration of the pool or
  *    matrix.  It is bit-identical in any batch, at any position in the batch
@@ -56,7 +61,7 @@ typedef enum {
   PKD_ERR_BOUNDS = 4,         /* index or count out of range: needed, available */
   PKD_ERR_DUPLICATE_PAGE = 5, /* a page id appears twice in one sequence's table */
   PKD_ERR_DEVICE = 6,         /* HIP runtime error; detail holds its text */
-  PKD_ERR_ROW = 7             /* pkd_pool_check: some row had an invalid (seq, pos) */
+  PKD_ERR_ROW = 7             /* pkd_pool_check: some row had an invalid (seq, pos) or table entry */
 } pkd_status;
 
 typedef struct {
@@ -174,7 +179,10 @@ size_t pkd_pool_bytes(const pkd_pool_desc* desc);
 /*
  * Lays a pool out in the caller's device buffer `dev_mem` of `bytes` bytes
  * (256-byte aligned): sets every block-table entry to -1, every count to 0
- * and the error word to 0 on `stream`.  Page contents are left as they are.
+ * and the error word to 0 on `stream`, and synchronises `stream` before
+ * returning, so that later calls on any stream see the laid-out pool.  Page
+ * contents are left as they are.  The handle keeps a host copy of the block
+ * tables (4 bytes per table entry).
  * Errors: PKD_ERR_INVALID_ARG, PKD_ERR_UNSUPPORTED (page_tokens != 32,
  * head_dim not 64/128, scales not 1 for a non-fp8 pool, non-finite or
  * non-positive fp8 scale), PKD_ERR_OUT_OF_MEMORY {needed, available} when
@@ -203,9 +211,10 @@ pkd_status pkd_pool_info_get(const pkd_pool* pool, pkd_pool_info* info);
  * above max_pages_per_seq {needed = count, available = max_pages_per_seq} or
  * a page id outside [0, num_pages) {needed = id, available = num_pages};
  * PKD_ERR_DUPLICATE_PAGE for a page listed twice in one sequence.
- * Synchronous: reads back the tables it replaces (to keep the per-page
- * sequence counts behind pkd_pool_info.shared_pages), writes the new ones and
- * returns after they have reached the device.
+ * The tables it replaces are taken from the handle's host copy (which keeps
+ * the per-page sequence counts behind pkd_pool_info.shared_pages); nothing is
+ * read back from the device.  Synchronous: writes the new tables on `stream`
+ * and returns after they have reached the device.
  */
 pkd_status block_table_set(pkd_pool* pool, int32_t first_seq, int32_t n_seqs,
                            const int32_t* pages_host, const int32_t* n_pages_host,
@@ -214,9 +223,13 @@ pkd_status block_table_set(pkd_pool* pool, int32_t first_seq, int32_t n_seqs,
 /*
  * Reads and clears the sticky device error word (synchronises `stream`).
  * Returns PKD_ERR_ROW if, since the last check, some launched row had a
- * sequence outside [0, max_seqs), a negative position, or a position at or
- * beyond 32 x (pages set for its sequence); such a row's outputs were written
- * as zeros and nothing was appended for it.  err->needed holds the bit set
+ * sequence outside [0, max_seqs), a negative position, a position at or
+ * beyond 32 x (pages set for its sequence), or a block-table entry among its
+ * pages outside [0, num_pages); such a row's outputs were written as zeros
+ * and nothing was appended for it.  The kernels check every table entry and
+ * page count they use (the device copies sit in caller memory at published
+ * offsets): an entry outside the pool is never dereferenced, and a count is
+ * taken as at most max_pages_per_seq.  err->needed holds the bits set
  * (1 = bad sequence, 2 = bad position, 4 = table entry outside the pool).
  */
 pkd_status pkd_pool_check(pkd_pool* pool, pkd_stream stream, pkd_error* err);

@@ -219,25 +219,40 @@ pkd_status kv_pool_create(const pkd_pool_desc* desc, void* dev_mem, size_t bytes
                 "pool needs %zu bytes, buffer has %zu", info.total_bytes, bytes);
   pkd_pool* p = (pkd_pool*)calloc(1, sizeof(pkd_pool));
   if (!p) return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)sizeof(pkd_pool), 0, "host allocation of the handle failed");
+  const int64_t tab = (int64_t)desc->max_seqs * desc->max_pages_per_seq;
   p->page_refs = (int32_t*)calloc((size_t)desc->num_pages, sizeof(int32_t));
-  if (!p->page_refs) {
+  p->host_table = (int32_t*)malloc(sizeof(int32_t) * (size_t)tab);
+  p->host_counts = (int32_t*)calloc((size_t)desc->max_seqs, sizeof(int32_t));
+  if (!p->page_refs || !p->host_table || !p->host_counts) {
+    free(p->page_refs);
+    free(p->host_table);
+    free(p->host_counts);
     free(p);
-    return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)desc->num_pages * 4, 0, "host allocation of page counts failed");
+    return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)desc->num_pages * 4 + tab * 4, 0,
+                "host allocation of the pool's table copy failed");
   }
+  for (int64_t i = 0; i < tab; ++i) p->host_table[i] = -1;
   p->desc = *desc;
   p->base = (uint8_t*)dev_mem;
   p->bytes = bytes;
   p->info = info;
   hipGetDevice(&p->device);
   hipStream_t st = (hipStream_t)stream;
-  const int64_t tab = (int64_t)desc->max_seqs * desc->max_pages_per_seq;
   hipLaunchKernelGGL(fill_i32_kernel, dim3(256), dim3(256), 0, st, (int32_t*)(p->base + info.table_offset), tab, -1);
   hipLaunchKernelGGL(fill_i32_kernel, dim3(64), dim3(256), 0, st, (int32_t*)(p->base + info.counts_offset),
                      (int64_t)desc->max_seqs, 0);
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, (int32_t*)(p->base + info.error_offset), 64, 0);
   pkd_status s = check_launch(err, "kv_pool_create");
+  // the fills land before the call returns, so that a later call on any
+  // stream (block_table_set included) sees the laid-out pool
+  if (s == PKD_OK) {
+    const hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) s = fail(err, PKD_ERR_DEVICE, 0, 0, "kv_pool_create: %s", hipGetErrorString(e));
+  }
   if (s != PKD_OK) {
     free(p->page_refs);
+    free(p->host_table);
+    free(p->host_counts);
     free(p);
     return s;
   }
@@ -246,7 +261,11 @@ pkd_status kv_pool_create(const pkd_pool_desc* desc, void* dev_mem, size_t bytes
 }
 
 pkd_status kv_pool_destroy(pkd_pool* pool) {
-  if (pool) free(pool->page_refs);
+  if (pool) {
+    free(pool->page_refs);
+    free(pool->host_table);
+    free(pool->host_counts);
+  }
   free(pool);
   return PKD_OK;
 }
@@ -290,25 +309,26 @@ pkd_status block_table_set(pkd_pool* pool, int32_t first_seq, int32_t n_seqs, co
   hipStream_t st = (hipStream_t)stream;
   int32_t* dt = (int32_t*)(pool->base + pool->info.table_offset) + (size_t)first_seq * mp;
   int32_t* dc = (int32_t*)(pool->base + pool->info.counts_offset) + first_seq;
-  // the tables being replaced, to keep the per-page sequence counts exact
-  std::vector<int32_t> old_table(table.size()), old_counts((size_t)n_seqs);
-  hipError_t e = hipMemcpyAsync(old_table.data(), dt, sizeof(int32_t) * table.size(), hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(old_counts.data(), dc, sizeof(int32_t) * (size_t)n_seqs, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e == hipSuccess) e = hipMemcpyAsync(dt, table.data(), sizeof(int32_t) * table.size(), hipMemcpyHostToDevice, st);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(dc, n_pages_host, sizeof(int32_t) * (size_t)n_seqs, hipMemcpyHostToDevice, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return fail(err, PKD_ERR_DEVICE, 0, 0, "block_table_set: %s", hipGetErrorString(e));
+  // The tables being replaced come from the handle's host copy (no read-back),
+  // which keeps the per-page sequence counts exact.
+  int32_t* ht = pool->host_table + (size_t)first_seq * mp;
+  int32_t* hc = pool->host_counts + first_seq;
   for (int32_t i = 0; i < n_seqs; ++i) {
-    for (int32_t j = 0; j < old_counts[i] && j < mp; ++j) {
-      const int32_t pg = old_table[(size_t)i * mp + j];
-      if (pg >= 0 && pg < d.num_pages && pool->page_refs[pg] > 0 && --pool->page_refs[pg] == 1) --pool->shared_pages;
+    for (int32_t j = 0; j < hc[i]; ++j) {
+      const int32_t pg = ht[(size_t)i * mp + j];
+      if (pool->page_refs[pg] > 0 && --pool->page_refs[pg] == 1) --pool->shared_pages;
     }
     for (int32_t j = 0; j < n_pages_host[i]; ++j)
       if (++pool->page_refs[table[(size_t)i * mp + j]] == 2) ++pool->shared_pages;
+    hc[i] = n_pages_host[i];
   }
+  memcpy(ht, table.data(), sizeof(int32_t) * table.size());
+  hipError_t e = hipMemcpyAsync(dt, ht, sizeof(int32_t) * table.size(), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(dc, hc, sizeof(int32_t) * (size_t)n_seqs, hipMemcpyHostToDevice, st);
+  // returns once the tables are on the device (the host copy may change with
+  // the next call)
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(err, PKD_ERR_DEVICE, 0, 0, "block_table_set: %s", hipGetErrorString(e));
   return ok(err);
 }
 

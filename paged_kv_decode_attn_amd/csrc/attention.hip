@@ -41,6 +41,7 @@ struct AttnParams {
   const int32_t* counts;
   int32_t max_pages;
   int32_t max_seqs;
+  int32_t num_pages;  // physical pages in the pool: a table entry outside [0, num_pages) is refused
   uint32_t* err;
   const int32_t* seq;
   const int32_t* pos;
@@ -68,8 +69,11 @@ struct AttnParams {
 
 // Chunk count of a row (0 for a refused row) and the record of its chunk c:
 // records are laid out per (row, chunk, kv head, query head of the group).
+__device__ __forceinline__ int seq_count(const AttnParams& P, int s) {
+  return (s >= 0 && s < P.max_seqs) ? min(P.counts[s], P.max_pages) : 0;
+}
 __device__ __forceinline__ int row_chunks(const AttnParams& P, int s, int p) {
-  if (s < 0 || s >= P.max_seqs || p < 0 || p >= kPage * P.counts[s]) return 0;
+  if (s < 0 || s >= P.max_seqs || p < 0 || p >= kPage * seq_count(P, s)) return 0;
   return ((p + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages;
 }
 __device__ __forceinline__ int64_t rec_of(const AttnParams& P, int r, int c, int g, int n) {
@@ -101,11 +105,22 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* p) { return *reinterpret_
 
 // First block-table window of sequence s (lane i: logical page i), read in
 // the same round trip as the page count; zeros for an out-of-range sequence.
+// The count is clamped to the table length, so that no row reads past its
+// sequence's table row whatever the device copy of the counts holds.
 __device__ __forceinline__ void row_meta(const AttnParams& P, int s, int& count, int& tab) {
   const bool s_ok = s >= 0 && s < P.max_seqs;
   const int l = lane_id();
-  count = s_ok ? P.counts[s] : 0;
+  count = s_ok ? min(P.counts[s], P.max_pages) : 0;
   tab = (s_ok && l < P.max_pages) ? P.table[(int64_t)s * P.max_pages + l] : 0;
+}
+
+// True (in every lane) when some lane l < n holds a table entry outside the
+// pool; such entries are replaced by page 0 in `tab`, so that no load or store
+// of the unit leaves the pool.  The unit is then refused (kErrPage).
+__device__ __forceinline__ bool refuse_window(const AttnParams& P, int n, int& tab) {
+  const bool b = lane_id() < n && (unsigned)tab >= (unsigned)P.num_pages;
+  tab = b ? 0 : tab;
+  return __builtin_amdgcn_ballot_w64(b) != 0;
 }
 
 // Row validity and context length; sets the sticky error word on a bad row.
@@ -477,8 +492,11 @@ __device__ __forceinline__ void append_store(const AttnParams& P, int g, int pag
 // other rows of the workgroup and were staged in LDS once for all of them
 // (page j's K block at staged + 2 j block_bytes, its V block after it); they
 // are read from there, byte for byte what the global loads would return.
+// Returns true when a table entry of the unit's pages lies outside the pool:
+// page 0 was read in its place and nothing was appended, and the caller
+// refuses the unit (zeros, kErrPage).
 template <int KVT, int D, bool FUSE = false>
-__device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, int r, int s, int p_row, int g,
+__device__ __forceinline__ bool run_unit(const AttnParams& P, Acc<KVT, D>& A, int r, int s, int p_row, int g,
                                          int pg0, int pg1, int tab, const QRegs<KVT, D>& qv,
                                          const QFRegs<KVT, D>& qf, const lds_u8* staged = nullptr,
                                          int n_staged = 0) {
@@ -493,10 +511,12 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
   // window at pg0): the unit's table entries arrive in one load instead of one
   // dependent load per page
   int win = pg0;
+  bool bad = refuse_window(P, pg1 - win, tab);
   auto page_of = [&](int pg) {
     if (pg - win >= kWave) {
       win += kWave;
       tab = win + lane_id() < pg1 ? trow[win + lane_id()] : 0;
+      bad = refuse_window(P, pg1 - win, tab) || bad;
     }
     return __shfl(tab, pg - win, kWave);
   };
@@ -507,8 +527,13 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
   const int own = FUSE ? p_row / kPage : -1;
   // the own page's table entry is read directly: the lane window above only
   // moves forward one page at a time, and the own page may lie 64 or more
-  // pages past pg0
-  const int own_page = FUSE ? trow[own] : 0;
+  // pages past pg0.  An entry outside the pool is not written to.
+  int own_page = FUSE ? trow[own] : 0;
+  const bool own_ok = !FUSE || (unsigned)own_page < (unsigned)P.num_pages;
+  if (!own_ok) {
+    own_page = 0;
+    bad = true;
+  }
   NewToken<KVT, D> nt;
   if constexpr (FUSE) append_load<KVT, D>(P, r, g, nt);
   u32x4 kr[GE::NL], vr[GE::NL];
@@ -518,12 +543,12 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
     else load_block<KVT, D>(base + (uint64_t)page_of(pg) * P.page_stride + c * P.block_bytes, regs);
   };
   if (FUSE && own == pg0) {
-    append_store<KVT, D>(P, g, own_page, p_row % kPage, nt);
+    if (own_ok) append_store<KVT, D>(P, g, own_page, p_row % kPage, nt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   load(pg0, 0, kr);
   load(pg0, 1, vr);
-  if (FUSE && own != pg0) append_store<KVT, D>(P, g, own_page, p_row % kPage, nt);
+  if (FUSE && own != pg0 && own_ok) append_store<KVT, D>(P, g, own_page, p_row % kPage, nt);
   for (int pg = pg0; pg < pg1; ++pg) {
     const bool nxt = pg + 1 < pg1;
     f32x4_t S[2];
@@ -537,6 +562,7 @@ __device__ __forceinline__ void run_unit(const AttnParams& P, Acc<KVT, D>& A, in
     page_pv<KVT, D>(vr, p, A.O);
     if (nxt) load(pg + 1, 1, vr);
   }
+  return bad;
 }
 
 // Sum of the lane-partial l over the four 16-lane groups (fixed butterfly).
@@ -698,7 +724,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
   int count, tab;
   row_meta(P, s, count, tab);
-  const bool ok = in_range && row_ok(P, s, p, count, g == 0);
+  bool ok = in_range && row_ok(P, s, p, count, g == 0);
+  // the row's first table window must name pool pages (the staging below
+  // reads the shared ones); later windows are checked as run_unit reaches them
+  if (ok && refuse_window(P, (p + kPage) / kPage, tab)) {
+    ok = false;
+    if (g == 0 && lane_id() == 0) atomicOr(P.err, kErrPage);
+  }
   int n_staged = 0;
   const lds_u8* staged = nullptr;
   if constexpr (STAGE) {
@@ -712,7 +744,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     return;
   }
   Acc<KVT, D> A;
-  run_unit<KVT, D, FUSE>(P, A, r, s, p, g, 0, (p + kPage) / kPage, tab, qv, qf, staged, n_staged);
+  if (run_unit<KVT, D, FUSE>(P, A, r, s, p, g, 0, (p + kPage) / kPage, tab, qv, qf, staged, n_staged)) {
+    if (lane_id() == 0) atomicOr(P.err, kErrPage);
+    zero_heads<D>(P, r, g);
+    return;
+  }
   finish<KVT, D>(P, A, r, g);
 }
 
@@ -742,20 +778,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float qf[GE::NQ];
   load_q<KVT, D>(P, r, g, qv, qf);
   if (P.tile_rows > 0 && tile_shared(P, r / P.tile_rows)) return;
-  const int count = (s >= 0 && s < P.max_seqs) ? P.counts[s] : 0;
+  const int count = seq_count(P, s);
   if (!row_ok(P, s, p, count, c == 0 && g == 0)) return;
   const int nch = (npg + P.chunk_pages - 1) / P.chunk_pages;
   if (c >= nch) return;
   const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
   const int tab = pg0 + l < pg1 ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
   Acc<KVT, D> A;
-  if (FUSE && c == nch - 1) run_unit<KVT, D, true>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf);
-  else run_unit<KVT, D, false>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf);
+  const bool bad = (FUSE && c == nch - 1) ? run_unit<KVT, D, true>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf)
+                                          : run_unit<KVT, D, false>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf);
+  if (bad && l == 0) atomicOr(P.err, kErrPage);
   if (nch == 1) {
-    finish<KVT, D>(P, A, r, g);
+    if (bad) zero_heads<D>(P, r, g);
+    else finish<KVT, D>(P, A, r, g);
     return;
   }
-  const float lsum = group_sum(A.l);
+  // a refused chunk leaves l = -1, which makes the merge zero the row
+  const float lsum = bad ? -1.0f : group_sum(A.l);
   if (n < P.G) {
     const int64_t rec = rec_of(P, r, c, g, n);
     if (grp == 0) {
@@ -791,7 +830,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const int r0 = t * P.tile_rows;
   const int s = P.seq[r0];
   const bool s_ok = s >= 0 && s < P.max_seqs;
-  const int count = s_ok ? P.counts[s] : 0;
+  const int count = seq_count(P, s);
   int rw[NB], hh[NB], pc[NB], nch[NB];
   bool live[NB], ok[NB];
   int pmax = -1;
@@ -835,10 +874,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   const uint8_t* base = P.pages + (uint64_t)g * 2 * P.block_bytes;
   int win = pg0;
   int tab = pg0 + l < pg1 ? trow[pg0 + l] : 0;
+  bool bad = refuse_window(P, pg1 - win, tab);
   auto page_of = [&](int pg) {
     if (pg - win >= kWave) {
       win += kWave;
       tab = win + l < pg1 ? trow[win + l] : 0;
+      bad = refuse_window(P, pg1 - win, tab) || bad;
     }
     return __shfl(tab, pg - win, kWave);
   };
@@ -870,14 +911,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     for (int b = 0; b < NB; ++b) page_pv<KVT, D>(vr, p[b], A[b].O);
     if (nxt) load(pg + 1, 1, vr);
   }
+  if (bad && l == 0) atomicOr(P.err, kErrPage);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const float lsum = group_sum(A[b].l);
+    // a refused chunk leaves l = -1, which makes the merge zero the row
+    const float lsum = bad ? -1.0f : group_sum(A[b].l);
     if (!act[b]) continue;
     if (nch[b] == 1) {
       const float inv = 1.0f / lsum;
 #pragma unroll
-      for (int mt = 0; mt < GE::NMT; ++mt) store_out4<D>(P, rw[b], hh[b], 16 * mt + 4 * grp, A[b].O[mt] * inv * P.v_scale);
+      for (int mt = 0; mt < GE::NMT; ++mt)
+        store_out4<D>(P, rw[b], hh[b], 16 * mt + 4 * grp,
+                      bad ? f32x4_t{0.f, 0.f, 0.f, 0.f} : A[b].O[mt] * inv * P.v_scale);
     } else {
       const int64_t rec = rec_of(P, rw[b], c, g, n % G);
       if (grp == 0) {
@@ -918,12 +963,20 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
       l0 = P.part_ml[2 * rec + 1];
     }
     float M = m0;
+    // a chunk that met a table entry outside the pool left l = -1: the row is
+    // refused and written as zeros
+    bool refused = l0 < 0.f;
     for (int c0 = kWave; c0 < nch; c0 += kWave)
-      if (c0 + l < nch) M = fmaxf(M, P.part_ml[2 * rec_of(P, r, c0 + l, g, n)]);
+      if (c0 + l < nch) {
+        const int64_t rec = rec_of(P, r, c0 + l, g, n);
+        M = fmaxf(M, P.part_ml[2 * rec]);
+        refused = refused || P.part_ml[2 * rec + 1] < 0.f;
+      }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
     float L = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += kWave) {
+    const int nsum = __builtin_amdgcn_ballot_w64(refused) ? 0 : nch;
+    for (int c0 = 0; c0 < nsum; c0 += kWave) {
       float wl = 0.f, ll = 0.f;
       if (c0 == 0) {
         if (l < nch) {
@@ -969,7 +1022,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
       if (cn <= 4) accumulate(std::integral_constant<int, 4>{});
       else accumulate(std::integral_constant<int, 16>{});
     }
-    const float inv = 1.0f / L;
+    const float inv = nsum ? 1.0f / L : 0.0f;
 #pragma unroll
     for (int j = 0; j < PER; ++j) o[j] = o[j] * inv * P.v_scale;
   }
@@ -991,11 +1044,16 @@ template <int KVT, int D>
 __global__ __launch_bounds__(64) void append_kernel(AttnParams P) {
   const int r = blockIdx.x / P.n_kv, g = blockIdx.x % P.n_kv;
   const int s = P.seq[r], p = P.pos[r];
-  const int count = (s >= 0 && s < P.max_seqs) ? P.counts[s] : 0;
+  const int count = seq_count(P, s);
   if (!row_ok(P, s, p, count, g == 0)) return;
+  const int page = P.table[(int64_t)s * P.max_pages + p / kPage];
+  if ((unsigned)page >= (unsigned)P.num_pages) {  // not written; the attention kernel refuses the row
+    if (g == 0 && lane_id() == 0) atomicOr(P.err, kErrPage);
+    return;
+  }
   NewToken<KVT, D> nt;
   append_load<KVT, D>(P, r, g, nt);
-  append_store<KVT, D>(P, g, P.table[(int64_t)s * P.max_pages + p / kPage], p % kPage, nt);
+  append_store<KVT, D>(P, g, page, p % kPage, nt);
 }
 
 // ------------------------------------------------------------------ host
@@ -1093,6 +1151,7 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   P.counts = (const int32_t*)(pool->base + pool->info.counts_offset);
   P.max_pages = d.max_pages_per_seq;
   P.max_seqs = d.max_seqs;
+  P.num_pages = d.num_pages;
   P.err = (uint32_t*)(pool->base + pool->info.error_offset);
   P.seq = a.seq;
   P.pos = a.pos;

@@ -90,6 +90,8 @@ struct pkd_pool {
   int device;
   int32_t* page_refs;    // host: sequences whose block table lists each physical page
   int64_t shared_pages;  // pages listed by two or more sequences
+  int32_t* host_table;   // host copy of the block tables [max_seqs][max_pages_per_seq] (-1 unset)
+  int32_t* host_counts;  // host copy of the page counts [max_seqs]
 };
 
 namespace pkd {

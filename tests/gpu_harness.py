@@ -30,15 +30,23 @@ def values(t: torch.Tensor, dtype: int) -> np.ndarray:
 
 
 class GpuPool:
-    def __init__(self, w: wl.Workload, chunk_pages: int | None = None, poison: bool = True):
+    """pad: bytes of guard memory (filled with 0xA5) allocated before and after
+    the pool's buffer, so that tests can check that nothing outside the pool
+    was written."""
+
+    def __init__(self, w: wl.Workload, chunk_pages: int | None = None, poison: bool = True, pad: int = 0):
         self.w = w
         chunk = w.attn_chunk_pages if chunk_pages is None else chunk_pages
         self.desc = pkd.pkd_pool_desc(w.num_pages, 32, w.n_kv, w.head_dim, w.kv_dtype, w.k_scale,
                                       w.v_scale, w.max_seqs, w.max_pages_per_seq, chunk)
         nbytes = pkd.pkd_pool_bytes(self.desc)
         assert nbytes > 0
-        self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=DEV)
-        off = (-self.mem.data_ptr()) % 256
+        pad = (pad + 255) // 256 * 256
+        self.mem = torch.empty(nbytes + 2 * pad + 256, dtype=torch.uint8, device=DEV)
+        if pad:
+            self.mem.fill_(0xA5)
+        off = (-self.mem.data_ptr()) % 256 + pad
+        self.pad = pad
         self.buf = self.mem[off:off + nbytes]
         self.handle = pkd.kv_pool_create(self.desc, self.buf)
         self.info = pkd.pkd_pool_info_get(self.handle)
@@ -51,6 +59,18 @@ class GpuPool:
         del hk, hv
         pkd.block_table_set(self.handle, 0, w.tables, w.counts)
         torch.cuda.synchronize()
+
+    def guard_intact(self) -> bool:
+        """The guard bytes around the pool still hold their fill."""
+        off = self.buf.data_ptr() - self.mem.data_ptr()
+        before, after = self.mem[:off], self.mem[off + self.buf.numel():]
+        return bool((before[off - self.pad:] == 0xA5).all()) and bool((after[:self.pad] == 0xA5).all())
+
+    def table_entries(self) -> torch.Tensor:
+        """The device copy of the block tables, int32 [max_seqs][max_pages_per_seq]."""
+        n = self.w.max_seqs * self.w.max_pages_per_seq
+        return self.buf[self.info.table_offset:self.info.table_offset + 4 * n].view(torch.int32).view(
+            self.w.max_seqs, self.w.max_pages_per_seq)
 
     def pages_bytes(self) -> torch.Tensor:
         w = self.w

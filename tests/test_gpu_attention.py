@@ -266,6 +266,59 @@ def test_invalid_rows_fused_append_and_flag_refusal(H):
     assert ei.value.status == 1
 
 
+TABLE_CASES = [
+    # lens, chunk, distinct, (bad sequence, its logical page), bad entry (0 = one past the pool, 1 = -1),
+    # first page shared by the sequences (the staging kernel)
+    ((100, 40, 70), 100, True, (0, 1), 0, False),     # one wave per row, fused append; first window
+    ((100, 40, 70), 100, True, (0, 3), 1, False),     # the row's own page
+    ((2600, 40, 70), 100, True, (0, 70), 0, False),   # a later window of a long row (reloaded in the page loop)
+    ((2600, 40, 70), 100, False, (0, 81), 1, False),  # own page of a long row; separate append kernel
+    ((100, 40, 70), 2, True, (0, 1), 1, False),       # page chunks, fused append in the last chunk, ordered merge
+    ((100, 40, 70), 2, False, (0, 3), 0, False),      # page chunks, separate append kernel, own page
+    ((100, 40, 70), 100, True, (2, 1), 0, True),      # shared leading pages staged in LDS
+]
+
+
+@pytest.mark.parametrize("lens,chunk,distinct,bad,kind,shared", TABLE_CASES)
+def test_table_entry_outside_pool(H, lens, chunk, distinct, bad, kind, shared):
+    """A block-table entry outside the pool, written into the device copy of
+    the table behind block_table_set: the kernels never dereference it (page 0
+    is read in its place and nothing outside the pool is written: the guard
+    bytes around the pool keep their fill), the row's outputs are zeros and
+    bit 4 of the error word is set; every other row keeps the bits of a
+    clean run, and the pool's pages change only where a clean run changes
+    them, plus possibly the bad row's own page."""
+    import paged_kv_decode_attn_amd as pkd
+    w = wl.make("attn", "cpu", seed=31, n_q=8, n_kv=2, d=128, kv_dtype=wl.BF16, lens=lens, append=True,
+                chunk=chunk, extra_pages=0, shared_first_page=shared)
+    s_bad, lp = bad
+    assert lp < int(w.counts[s_bad])
+    args = (w.seq, w.pos, w.q.cuda(), w.k_new.cuda(), w.v_new.cuda(), wl.F32, distinct)
+    clean_pool = H.GpuPool(w)
+    clean = H.run_attention(clean_pool, *args).cpu()
+    pkd.pkd_pool_check(clean_pool.handle)
+    assert (pkd.pkd_pool_info_get(clean_pool.handle).shared_pages > 0) == shared
+    page_bytes = 2 * w.n_kv * clean_pool.info.block_bytes
+    pool = H.GpuPool(w, pad=2 * page_bytes)
+    pool.table_entries()[s_bad, lp] = w.num_pages if kind == 0 else -1
+    torch.cuda.synchronize()
+    out = H.run_attention(pool, *args).cpu()
+    with pytest.raises(pkd.PkdError) as ei:
+        pkd.pkd_pool_check(pool.handle)
+    assert ei.value.status == 7 and ei.value.needed & 4
+    assert pool.guard_intact()
+    r_bad = int(np.nonzero(w.seq == s_bad)[0][0])
+    assert (out[r_bad] == 0).all()
+    others = [r for r in range(w.n_rows) if r != r_bad]
+    assert torch.equal(out[others].view(torch.int32), clean[others].view(torch.int32))
+    own = int(w.tables[s_bad][int(w.pos[r_bad]) // 32])
+    a = pool.pages_bytes().view(w.num_pages, -1).cpu()
+    b = clean_pool.pages_bytes().view(w.num_pages, -1).cpu()
+    keep = [pg for pg in range(w.num_pages) if pg != own]
+    assert torch.equal(a[keep], b[keep])
+    pkd.pkd_pool_check(pool.handle)  # cleared
+
+
 def test_block_table_refusals(H):
     import paged_kv_decode_attn_amd as pkd
     w = wl.make("attn", "cpu", seed=8, n_q=4, n_kv=2, d=64, kv_dtype=wl.F32, lens=(20, 40), append=False,

@@ -244,7 +244,7 @@ def full_case(H, orc, name, kw, rows_fn, device="cpu", norm_rope=False):
         w = wl.with_norm_rope(w)
     label = f"{w.name} ({w.n_rows} rows, family {w.family})"
     print(f"workload {label}", flush=True)
-    hint = w.n_rows if w.family in (wl.MFMA, 2) else None
+    hint = w.n_rows if w.family in (wl.MFMA, wl.MFMA_FP8) else None
     layer = H.GpuLayer(w, batch_hint=hint)
     rows = rows_fn(w)
     o, res = run_stages(H, orc, w, layer, rows, label)
@@ -296,6 +296,7 @@ NORM_ROPE_CASES = [
     ("0.6b-mixed-bf16", dict(n_decode=48, chunk_rows=24, chunk=4, long_max=1400)),
     ("0.6b-mixed-bf16", dict(n_decode=48, chunk_rows=24, chunk=4, long_max=1400, family=wl.GEMV)),
     ("7b-b4096-fp8", dict(n=64, L=100)),
+    ("7b-b4096-fp8", dict(n=64, L=100, family=wl.MFMA)),
 ]
 
 

@@ -21,7 +21,7 @@ import numpy as np
 import torch
 
 F32, BF16, FP8 = 0, 1, 2
-GEMV, MFMA = 0, 1
+GEMV, MFMA, MFMA_FP8 = 0, 1, 2
 ESIZE = {F32: 4, BF16: 2, FP8: 1}
 TORCH_CODE = {F32: torch.float32, BF16: torch.int16, FP8: torch.uint8}
 
@@ -332,11 +332,13 @@ def _b768_7b(gen, rng, dev, n: int = 768, family: int = MFMA, chunk: int = 8,
                     notes="shared physical pages: 2 per sequence")
 
 
-def _b4096_fp8(gen, rng, dev, n: int = 4096, L: int = 1024, family: int = MFMA,
+def _b4096_fp8(gen, rng, dev, n: int = 4096, L: int = 1024, family: int = MFMA_FP8,
                with_weights: bool = True):
     """7B-class layer, batch 4096, fp8: E4M3 weights (per-tensor scales) and KV
     (scales max|v| / 448 over the history), contexts of L tokens in 32-token
-    pages placed by a random permutation of the whole pool."""
+    pages placed by a random permutation of the whole pool.  The projections
+    run as native fp8 matrix-core contractions (family 2) unless `family`
+    says otherwise."""
     D, nq, nkv, d, F = 3584, 28, 4, 128, 18944
     ws, sc = ({}, {})
     if with_weights:
