@@ -303,6 +303,26 @@ pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_h
                              void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
                              pkd_stream stream, pkd_error* err);
 
+/*
+ * paged_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, semantics, kernels and results (bit for bit)
+ * as paged_attn_decode, without the workspace: the chunk records of chunked
+ * pools go to a fixed scratch array of pkd_attn_noalloc_scratch_bytes()
+ * (64 MiB) in device memory, which every GPU the library runs on holds from
+ * the first such call until the process ends.  The call allocates nothing.
+ * A call needing more than the scratch (pkd_attn_workspace_bytes of the same
+ * arguments) is refused with PKD_ERR_OUT_OF_MEMORY {needed, available}
+ * before anything is launched.  No part of the scratch has to start at zero:
+ * every record a call reads is written by the same call.  Every call on one
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ * streams, other threads) race and must not be made.
+ */
+size_t pkd_attn_noalloc_scratch_bytes(void);
+pkd_status paged_attn_decode_noalloc(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_heads,
+                                     const void* q, const void* k_new, const void* v_new, void* out,
+                                     int32_t out_dtype, pkd_stream stream, pkd_error* err);
+
 /* ------------------------------------------------------------------------ */
 /* Weight matrix-vector products                                             */
 /* ------------------------------------------------------------------------ */

@@ -85,7 +85,8 @@ LAYER_NORM, LAYER_ROPE = 1, 2
 
 
 EXPORTS = ["pkd_pool_bytes", "kv_pool_create", "kv_pool_destroy", "pkd_pool_info_get", "block_table_set",
-           "pkd_pool_check", "pkd_attn_workspace_bytes", "paged_attn_decode", "pkd_gemv_workspace_bytes",
+           "pkd_pool_check", "pkd_attn_workspace_bytes", "paged_attn_decode", "pkd_attn_noalloc_scratch_bytes",
+           "paged_attn_decode_noalloc", "pkd_gemv_workspace_bytes",
            "pkd_suggest_k_splits", "gemv_rows", "gemv_gather_rows", "rms_norm_factor", "rope_table",
            "pkd_step_workspace_bytes", "decode_step", "pkd_status_string", "pkd_version"]
 
@@ -106,6 +107,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkd_pool_check": (I32, [P, P, E]),
         "pkd_attn_workspace_bytes": (SZ, [P, I32, I32]),
         "paged_attn_decode": (I32, [P, ctypes.POINTER(pkd_rows), I32, P, P, P, P, I32, P, SZ, P, E]),
+        "pkd_attn_noalloc_scratch_bytes": (SZ, []),
+        "paged_attn_decode_noalloc": (I32, [P, ctypes.POINTER(pkd_rows), I32, P, P, P, P, I32, P, E]),
         "pkd_gemv_workspace_bytes": (SZ, [ctypes.POINTER(pkd_matrix), I32]),
         "pkd_suggest_k_splits": (I32, [I32, I32, I32, I32]),
         "gemv_rows": (I32, [ctypes.POINTER(pkd_matrix), P, I32, I32, P, ctypes.POINTER(pkd_epilogue), P, SZ,
@@ -211,6 +214,18 @@ def paged_attn_decode(pool, rows: pkd_rows, n_q_heads: int, q, k_new, v_new, out
     _check(lib().paged_attn_decode(pool, ctypes.byref(rows), n_q_heads, _ptr(q), _ptr(k_new), _ptr(v_new),
                                    _ptr(out), out_dtype, _ptr(ws), ws_bytes, _stream(stream),
                                    ctypes.byref(err)), err)
+
+
+def pkd_attn_noalloc_scratch_bytes() -> int:
+    return lib().pkd_attn_noalloc_scratch_bytes()
+
+
+def paged_attn_decode_noalloc(pool, rows: pkd_rows, n_q_heads: int, q, k_new, v_new, out, out_dtype: int,
+                              stream=None) -> None:
+    """paged_attn_decode with the library's fixed per-GPU scratch instead of a workspace."""
+    err = pkd_error()
+    _check(lib().paged_attn_decode_noalloc(pool, ctypes.byref(rows), n_q_heads, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                           _ptr(out), out_dtype, _stream(stream), ctypes.byref(err)), err)
 
 
 # ------------------------------------------------------------------ projections

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -236,7 +237,7 @@ pkd_status kv_pool_create(const pkd_pool_desc* desc, void* dev_mem, size_t bytes
   p->base = (uint8_t*)dev_mem;
   p->bytes = bytes;
   p->info = info;
-  hipGetDevice(&p->device);
+  (void)hipGetDevice(&p->device);
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(fill_i32_kernel, dim3(256), dim3(256), 0, st, (int32_t*)(p->base + info.table_offset), tab, -1);
   hipLaunchKernelGGL(fill_i32_kernel, dim3(64), dim3(256), 0, st, (int32_t*)(p->base + info.counts_offset),
@@ -392,6 +393,77 @@ pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_h
   a.out_dtype = out_dtype;
   a.out_stride = (int64_t)n_q_heads * d;
   return attn_launch(a, ws, ws_bytes, (hipStream_t)stream, err);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation attention
+// Scratch of paged_attn_decode_noalloc: the chunk records of chunked pools,
+// in a fixed device array that every GPU the library runs on holds for the
+// life of the process.  Host code never uses the array's name as an address:
+// its device address is looked up once per device (with that device current)
+// and kept in scratch_dev.
+namespace pkd {
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace pkd
+static __device__ __align__(256) uint8_t scratch[pkd::kNoAllocScratchBytes];
+static void* scratch_dev[pkd::kMaxDevices];
+static std::mutex scratch_mu;
+
+static pkd_status scratch_address(void** out, pkd_error* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(err, PKD_ERR_DEVICE, 0, 0, "paged_attn_decode_noalloc: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(err, PKD_ERR_UNSUPPORTED, dev, kMaxDevices, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(err, PKD_ERR_DEVICE, 0, 0, "paged_attn_decode_noalloc: scratch address: %s", hipGetErrorString(e));
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return PKD_OK;
+}
+
+extern "C" {
+
+size_t pkd_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+pkd_status paged_attn_decode_noalloc(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_heads, const void* q,
+                                     const void* k_new, const void* v_new, void* out, int32_t out_dtype,
+                                     pkd_stream stream, pkd_error* err) {
+  pkd_status s = validate_attn(pool, rows, n_q_heads, q, k_new, v_new, out, out_dtype, err);
+  if (s != PKD_OK) return s;
+  const size_t need = attn_workspace_bytes(pool, n_q_heads, rows->n);
+  if (need > kNoAllocScratchBytes)
+    return fail(err, PKD_ERR_OUT_OF_MEMORY, (int64_t)need, (int64_t)kNoAllocScratchBytes,
+                "paged_attn_decode_noalloc: %d rows need %zu bytes of chunk records, more than its fixed "
+                "%zu-byte scratch; use paged_attn_decode with a workspace",
+                rows->n, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && (s = scratch_address(&ws, err)) != PKD_OK) return s;
+  const int d = pool->desc.head_dim;
+  AttnArgs a{};
+  a.pool = pool;
+  a.seq = rows->seq;
+  a.pos = rows->pos;
+  a.distinct = (rows->flags & PKD_ROWS_DISTINCT_SEQS) != 0;
+  a.n_rows = rows->n;
+  a.n_q_heads = n_q_heads;
+  a.q = q;
+  a.q_stride = (int64_t)n_q_heads * d;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.kv_new_stride = (int64_t)pool->desc.num_kv_heads * d;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.out_stride = (int64_t)n_q_heads * d;
+  return attn_launch(a, ws, need > 0 ? kNoAllocScratchBytes : 0, (hipStream_t)stream, err);
 }
 
 size_t pkd_gemv_workspace_bytes(const pkd_matrix* W, int32_t max_rows) { return proj_workspace_bytes(W, max_rows); }
