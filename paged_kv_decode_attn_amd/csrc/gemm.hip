@@ -82,7 +82,10 @@ struct Tile {
   static constexpr int KB = 128;
   static constexpr int STAGE_BYTES = (TN + TM) * KB;
   static constexpr int STAGES = MODE == 1 ? 2 : (TM == 256 ? 2 : 3);
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;            // at most 144 KiB
+  // bf16, TM = 256: the weight part of a stage has three buffers and the
+  // activation part two (the weights are requested two stages ahead), 160 KiB
+  static constexpr bool WRING = MODE == 0 && TM == 256;
+  static constexpr int LDS_BYTES = WRING ? 3 * TN * KB + 2 * TM * KB : STAGES * STAGE_BYTES;
   static constexpr int DPW = STAGE_BYTES / 1024 / NWAVES;            // 1 KiB wave loads per stage
   static constexpr int RPB = 1024 / KB;                              // LDS rows per 1 KiB block
   static constexpr int MW = TM / 64;                                 // waves along the activation rows
@@ -325,29 +328,56 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     // before the loop), into the buffer of stage t - 1, which both groups
     // finished reading before A's M(t) began; A waits for it at the end of its
     // C(t), so the barrier that opens M(t + 1) publishes it.
-    static_assert(STAGES == 2 && DPW == 8, "two stages of 64 blocks");
+    // The weight half of stage t sits in weight buffer t % 3 and the
+    // activation half in activation buffer t % 2.  Waves 0, 1 load weights,
+    // waves 2, 3 activations: at the start of A's M(t), stage t + 2's weights
+    // and stage t + 1's activations, each into the buffer of stage t - 1,
+    // which both groups finished reading before A's M(t) began.  So the
+    // weights (the operand that misses L2: each block is read by the few row
+    // tiles that share it) have four phases to land, the activations two.  A
+    // wave waits at the end of its C(t) for its part of stage t + 1 only.
+    static_assert(STAGES == 2 && DPW == 8 && T::WRING, "weight ring of three, activation ring of two");
     const bool grp_b = wave_u >= 4;
+    const bool w_loader = wave_u < 2;
     u32x4 wo0[WA], xo0[4], wo1[WA], xo1[4];
-    // A wave w fills LDS rows 128 w .. 128 w + 127 (blocks 16 w .. 16 w + 15):
-    // two runs of 64 consecutive global rows (gate and up halves of a slab
-    // under silu), each starting at a wave-uniform row.
+    constexpr int WBUF = TN * KB, XBUF = TM * KB;
+    uint8_t* const wring = smem;
+    uint8_t* const xring = smem + 3 * WBUF;
+    // An A wave w fills LDS rows 128 (w % 2) .. + 127 of the weight part (w < 2)
+    // or of the activation part (w = 2, 3): two runs of 64 consecutive global
+    // rows (gate and up halves of a slab under silu), each starting at a
+    // wave-uniform row.
     const uint32_t run0 = (uint32_t)block_row(16 * (wave_u & 3)) * (uint32_t)kbytes;
     const uint32_t run1 = (uint32_t)block_row(16 * (wave_u & 3) + 8) * (uint32_t)kbytes;
     const uint32_t blk_stride = 8 * (uint32_t)kbytes;
-    const __amdgpu_buffer_rsrc_t aview = wave_u < 2 ? wview : xview;
+    const __amdgpu_buffer_rsrc_t aview = w_loader ? wview : xview;
     auto dma_a = [&](int kt) {
-      uint8_t* base = smem + (kt % 2) * SB + 16 * 1024 * wave_u;
+      uint8_t* base = (w_loader ? wring + (kt % 3) * WBUF : xring + (kt % 2) * XBUF) + 16 * 1024 * (wave_u & 1);
       const uint32_t koff = (uint32_t)(kt0 + kt) * KT_BYTES;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         lds_load16(aview, voff, (i < 8 ? run0 : run1) + (uint32_t)(i & 7) * blk_stride + koff, base + 1024 * i);
     };
+    // operands of k-step h of stage kt, as read_ops, from the two rings
+    auto read_ring = [&](int kt, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) {
+      const uint8_t* w = wring + (kt % 3) * WBUF;
+      const uint8_t* x = xring + (kt % 2) * XBUF;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xo[c] = *reinterpret_cast<const u32x4*>(x + swz<KB>(wm * 64 + 16 * c + i16, 4 * h + grp));
+#pragma unroll
+      for (int a = 0; a < WA; ++a) wo[a] = *reinterpret_cast<const u32x4*>(w + swz<KB>(wn * WN + 16 * a + i16, 4 * h + grp));
+    };
     if (!grp_b && nk > 0) {
-      dma_a(0);
-      if (nk > 1) {
-        dma_a(1);
-        __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
+      if (w_loader) {
+        dma_a(0);
+        if (nk > 1) {
+          dma_a(1);
+          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
+        } else {
+          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+        }
       } else {
+        dma_a(0);
         __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
       }
     }
@@ -355,10 +385,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     if (grp_b) lds_barrier();
     for (int kt = 0; kt < nk; ++kt) {
       // M(kt)
-      if (!grp_b && kt >= 1 && kt + 1 < nk) dma_a(kt + 1);
-      const uint8_t* cur = smem + (kt % 2) * SB;
-      read_ops(cur, 0, wo0, xo0);
-      read_ops(cur, 1, wo1, xo1);
+      const int ahead = w_loader ? kt + 2 : kt + 1;
+      const bool issued = !grp_b && ahead < nk;
+      if (issued) dma_a(ahead);
+      read_ring(kt, 0, wo0, xo0);
+      read_ring(kt, 1, wo1, xo1);
       wait_lds_reads();
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
@@ -366,7 +397,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       // C(kt)
       mma(wo0, xo0);
       mma(wo1, xo1);
-      if (!grp_b) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+      // this wave's part of stage kt + 1 has landed (a weight loader may still
+      // have stage kt + 2's 16 loads in flight)
+      if (!grp_b) {
+        if (w_loader && issued) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
+        else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+      }
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);

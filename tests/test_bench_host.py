@@ -54,6 +54,33 @@ def test_projection_flops_and_gate_up_bytes_by_hand():
     assert st["gate_up"] == 32768 + 384 + 768
 
 
+def test_implementation_passes_not_counted():
+    """The bf16 cast of x, the bf16 copy of h and K-split partial sums are the
+    implementation's, not the method's: only weights, inputs, outputs and
+    residual reads are counted."""
+    st, _, _ = bench.step_bytes(_tiny(), ELEM)
+    assert "cast" not in st
+    # W_o: weights 64 x 64 bf16, attn 3 x 64 bf16, residual x read and h written in f32
+    assert st["wo"] == 64 * 64 * 2 + 3 * 64 * 2 + 3 * 64 * 4 * 2
+    # qkv: weights 128 x 64, x in the activation dtype, qkv out
+    assert st["qkv"] == 128 * 64 * 2 + 3 * 64 * 2 + 3 * 128 * 2
+    # the append writes each row's key and value once
+    assert st["append"] == 3 * 2 * 2 * 16 * 2
+
+
+def test_stage_roofline():
+    # attention: HBM; fp8 matrix cores for family 2, bf16 for families 1 and 3, vector ALU for 0
+    assert bench.stage_peak("attention", -1, 1) == ("hbm", None)
+    assert bench.stage_peak("gate_up", 2, 2) == ("mfma", 5000.0)
+    assert bench.stage_peak("gate_up", 1, 2) == ("mfma", 2500.0)
+    assert bench.stage_peak("qkv", 3, 1) == ("mfma", 2500.0)
+    assert bench.stage_peak("qkv", 0, 1) == ("alu", 157.3)
+    # 8 GB at 8 TB/s = 1 ms; 5 PFLOP at 2.5 PF = 2 s: the larger wins
+    assert abs(bench.ideal_us(8e9, 0, None) - 1e3) < 1e-9
+    assert abs(bench.ideal_us(8e9, 5e15, 2500.0) - 2e6) < 1e-6
+    assert abs(bench.ideal_us(8e9, 1e9, 2500.0) - 1e3) < 1e-9
+
+
 def test_traffic_figure_used_only_for_its_sources(monkeypatch):
     got = bench.measured_traffic("gate_up", "7b-b768-prefix-bf16", 1)
     path = os.path.join(ROOT, "profiles", "gate_up_7b-b768-prefix-bf16.traffic.txt")

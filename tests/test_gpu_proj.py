@@ -167,13 +167,14 @@ def test_mfma_parity(H, orc, fam, wdt, xdt, rows, cols, n, silu, res, out, S):
     assert H.rel_err(H.values(yb, wl.BF16)[idx], want) <= TOL_BF16
 
 
-@pytest.mark.parametrize("k_splits", [1, 2])
-def test_mfma_tile_height_invariance(H, k_splits):
+@pytest.mark.parametrize("cols,k_splits", [(512, 1), (512, 2), (64, 1), (128, 1), (192, 1), (192, 2), (320, 3)])
+def test_mfma_tile_height_invariance(H, cols, k_splits):
     """A large batch runs on the 256-row activation tile (2,048 rows over 64
     weight tiles: two rounds of 256-row tiles against four of 128-row ones) and
     a small one on the 128-row tile; a row's outputs are bit-identical either
-    way, with and without a K split."""
-    rows, cols, n_all = 16384, 512, 2048
+    way, with and without a K split, down to K ranges of one to five 64-wide
+    k-steps (the first and last stages of the tile's load pipeline)."""
+    rows, n_all = 16384, 2048
     W, s = make_w(rows, cols, wl.BF16, 11)
     x = make_x(n_all, cols, wl.BF16, 12)
     full, _ = run_proj(H, W, rows, cols, wl.BF16, 1.0, 1, x, wl.BF16, n_all, wl.F32, k_splits=k_splits)
