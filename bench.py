@@ -43,6 +43,9 @@ def parse(argv=None):
     ap.add_argument("--workload", default="7b-b768-prefix-bf16")
     ap.add_argument("--configs", default="all",
                     help="workloads measured besides the headline one: all, none, or a comma list")
+    ap.add_argument("--sections", default="all",
+                    help="parts to run: all, or a comma list of step, norm_rope, t1, t2, head, prefill, configs, cpu "
+                         "(a profile of one part)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-t2", action="store_true", help="skip the small-batch GEMV pass")
     ap.add_argument("--no-head", action="store_true", help="skip the output-head (candidate rows) pass")
@@ -167,16 +170,17 @@ def measured_traffic(stage: str, workload: str, family: int):
 
 
 def traced_us(stage: str, workload: str, family: int):
-    """Average duration of the stage's kernel(s) per step in the committed
-    rocprofv3 kernel trace of this workload's step, or None if there is none
-    or the kernel source changed since it was taken."""
+    """Average duration of the stage's kernel(s) in the committed rocprofv3
+    kernel trace of this workload's step (the stage alone, launched back to
+    back, where the trace has it), or None if there is none or the kernel
+    source changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"step_{workload}.stages.txt")
     if not os.path.exists(path):
         return None
     kv = _kv_file(path)
     if kv.get(f"{stage}_source_sha256") != source_hash(stage, family):
         return None
-    v = kv.get(f"{stage}_us_per_step")
+    v = kv.get(f"{stage}_us_alone") or kv.get(f"{stage}_us_per_step")
     return float(v) if v else None
 
 
@@ -388,20 +392,30 @@ class Bench:
                              "TFLOP_s": round(fl / us / 1e6, 1) if fl else None,
                              "bound": bound, "ideal_us": round(ideal, 2), "roofline_frac": round(ideal / us, 4)}
         dom = max(stage_us, key=stage_us.get)
+        # the dominant stage alone, launched back to back between two events:
+        # its kernels' average duration without an event pair around each launch
+        dom_fn = dict(stages)[dom]
+        e0.record(stream)
+        for _ in range(args.steps):
+            dom_fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dom_us = e0.elapsed_time(e1) / args.steps * 1e3
+        pkd.pkd_pool_check(pool.handle)
         bound, peak = stage_peak(dom, int(fams[dom]), w.w_dtype)
         if bound == "hbm" or (bound == "alu" and sbytes_m[dom] / (HBM_PEAK_GBS * 1e9) >=
                               sflops.get(dom, 0) / (peak * 1e12)):
             bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
-            achieved = sbytes_m[dom] / stage_us[dom] / 1e3
+            achieved = sbytes_m[dom] / dom_us / 1e3
         else:
             unit = "TFLOP/s"
-            achieved = sflops[dom] / stage_us[dom] / 1e6
+            achieved = sflops[dom] / dom_us / 1e6
         fam = int(fams[dom]) if dom != "attention" else 0
         tr_us = traced_us(dom, w.name, fam)
         roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, w.name, fam),
-                    "algorithmic_bytes": int(sbytes_m[dom]), "us": round(stage_us[dom], 2),
-                    "trace_us": tr_us}
+                    "algorithmic_bytes": int(sbytes_m[dom]), "us": round(dom_us, 2),
+                    "us_between_stages": round(stage_us[dom], 2), "trace_us": tr_us}
         rec = {"rows": B, "dtype": {0: "f32", 1: "bf16", 2: "fp8"}[w.w_dtype], "projection_family": int(L.w_qkv.family),
                "us_per_step": round(mean, 2), "median_us": round(med, 2), "p10_us": round(p10, 2),
                "p90_us": round(p90, 2), "us_per_step_eager": round(us_eager, 2),
@@ -645,21 +659,39 @@ def main():
     import torch
     import workloads as wl
 
+    allp = {"step", "norm_rope", "t1", "t2", "head", "prefill", "configs", "cpu"}
+    sec = allp if args.sections == "all" else set(args.sections.split(","))
+    if sec - allp:
+        print(f"unknown sections {sorted(sec - allp)}", file=sys.stderr)
+        sys.exit(2)
     torch.cuda.set_device(0)
     bench = Bench(args)
+    for flag, part in (("no_norm_rope", "norm_rope"), ("no_t2", "t2"), ("no_head", "head"),
+                       ("no_prefill", "prefill"), ("no_cpu_baseline", "cpu")):
+        if getattr(args, flag):
+            sec.discard(part)
+    if args.configs == "none":
+        sec.discard("configs")
     kw = {} if args.family is None else {"family": args.family}
     log(f"generating workload {args.workload}")
     w = wl.make(args.workload, "cuda", **kw)
-    rec, ctx = bench.measure(w, detail=True)
-    nr = None if args.no_norm_rope else bench.norm_rope_step(w, ctx)
-    t1 = bench.t1(ctx)
-    total_bytes = ctx["total_bytes"]
-    del ctx
-    t2 = bench.t2(w) if (not args.no_t2 and w.ffn and w.w_dtype == 1) else None
-    head = None if args.no_head else bench.head()
-    pre = bench.prefill(w) if (not args.no_prefill and w.w_dtype == 1 and w.ffn) else None
+    rec = ctx = nr = t1 = None
+    total_bytes = None
+    if sec & {"step", "norm_rope", "t1", "cpu"}:
+        rec, ctx = bench.measure(w, detail=True)
+        total_bytes = ctx["total_bytes"]
+        nr = bench.norm_rope_step(w, ctx) if "norm_rope" in sec else None
+        t1 = bench.t1(ctx) if "t1" in sec else None
+        del ctx
+    t2 = bench.t2(w) if ("t2" in sec and w.ffn and w.w_dtype == 1) else None
+    head = bench.head() if "head" in sec else None
+    pre = bench.prefill(w) if ("prefill" in sec and w.w_dtype == 1 and w.ffn) else None
+    if rec is None:  # a profile of one part: no step line
+        print(json.dumps({"t2_gemv": t2, "output_head": head, "prefill": pre}))
+        return
     configs = {w.name: {k: v for k, v in rec.items() if k not in ("kernels",)}}
-    names = CONFIG_WORKLOADS if args.configs == "all" else ([] if args.configs == "none" else args.configs.split(","))
+    names = [] if "configs" not in sec else (
+        CONFIG_WORKLOADS if args.configs == "all" else args.configs.split(","))
     for name in names:
         if name == w.name:
             continue
@@ -669,7 +701,7 @@ def main():
         configs[name] = rc
         del wc
         torch.cuda.empty_cache()
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, total_bytes, args.cpu_max_s)
+    cpu = cpu_baseline(w, total_bytes, args.cpu_max_s) if "cpu" in sec else None
     line = {
         "metric": "decode-step us and achieved HBM GB/s (% of peak), paged attn + GEMV",
         "value": rec["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
