@@ -383,11 +383,27 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     }
     lds_barrier();
     if (grp_b) lds_barrier();
+    // Stacked gate/up matrices: the weight loaders also request the weight
+    // lines of stage t + PF into L2 (one dword per lane and row run), so that
+    // stage's loads into LDS find them there.  The values are folded into
+    // pf_acc, read once the wait below has retired them, and consumed after
+    // the loop under a condition that never holds.  Measured: gate/up 3-9%
+    // faster at batches 256 to 4,096; on the down and qkv shapes the same
+    // prefetch cost 3-4%, so it is used for silu-pair matrices only.
+    constexpr int PF = 6;
+    unsigned pf_acc = 0, pf_prev0 = 0, pf_prev1 = 0;
     for (int kt = 0; kt < nk; ++kt) {
       // M(kt)
       const int ahead = w_loader ? kt + 2 : kt + 1;
       const bool issued = !grp_b && ahead < nk;
       if (issued) dma_a(ahead);
+      const bool pf = w_loader && !grp_b && P.silu && kt + PF < nk;
+      unsigned pf0 = 0, pf1 = 0;
+      if (pf) {
+        const uint32_t koffp = (uint32_t)(kt0 + kt + PF) * KT_BYTES;
+        pf0 = __builtin_amdgcn_raw_buffer_load_b32(wview, (uint32_t)(l * kbytes), run0 + koffp, 0);
+        pf1 = __builtin_amdgcn_raw_buffer_load_b32(wview, (uint32_t)(l * kbytes), run1 + koffp, 0);
+      }
       read_ring(kt, 0, wo0, xo0);
       read_ring(kt, 1, wo1, xo1);
       wait_lds_reads();
@@ -398,16 +414,25 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       mma(wo0, xo0);
       mma(wo1, xo1);
       // this wave's part of stage kt + 1 has landed (a weight loader may still
-      // have stage kt + 2's 16 loads in flight)
+      // have stage kt + 2's 16 loads and this stage's 2 prefetches in flight)
       if (!grp_b) {
-        if (w_loader && issued) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
-        else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+        if (w_loader && issued) {
+          if (pf) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(18));
+          else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
+        } else {
+          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+        }
       }
+      pf_acc ^= pf_prev0 ^ pf_prev1;
+      pf_prev0 = pf0;
+      pf_prev1 = pf1;
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!grp_b) lds_barrier();
+    pf_acc ^= pf_prev0 ^ pf_prev1;
+    if (pf_acc == 0x9e3779b9u && P.M < 0) reinterpret_cast<float*>(P.y)[0] = 0.f;
   } else if constexpr (MODE == 0) {
     // Ping-pong over the KS = KB / 64 k-steps of each stage: the operands of
     // step g + 1 are read into one register set while the products of step g
