@@ -83,7 +83,9 @@ struct Tile {
   static constexpr int STAGE_BYTES = (TN + TM) * KB;
   static constexpr int STAGES = MODE == 1 ? 2 : (TM == 256 ? 2 : 3);
   // bf16, TM = 256: the weight part of a stage has three buffers and the
-  // activation part two (the weights are requested two stages ahead), 160 KiB
+  // activation part two (the weights are requested two stages ahead), 160 KiB.
+  // (The same ring on the native fp8 tile measured 6-20% slower on every fp8
+  // projection, so that tile keeps two whole stages.)
   static constexpr bool WRING = MODE == 0 && TM == 256;
   static constexpr int LDS_BYTES = WRING ? 3 * TN * KB + 2 * TM * KB : STAGES * STAGE_BYTES;
   static constexpr int DPW = STAGE_BYTES / 1024 / NWAVES;            // 1 KiB wave loads per stage
@@ -247,14 +249,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
   // bf16 operands of k-step h (of two 32-wide steps per stage): the wave's WA
   // weight tiles and 4 activation tiles, row i16 of each 16-row tile, 16 bytes
   // at k-chunk 4 h + grp.
-  auto read_ops = [&](const uint8_t* s, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) {
-    const uint8_t* w = s;
-    const uint8_t* x = s + TN * KB;
+  auto read_ops2 = [&](const uint8_t* w, const uint8_t* x, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) xo[c] = *reinterpret_cast<const u32x4*>(x + swz<KB>(wm * 64 + 16 * c + i16, 4 * h + grp));
 #pragma unroll
     for (int a = 0; a < WA; ++a) wo[a] = *reinterpret_cast<const u32x4*>(w + swz<KB>(wn * WN + 16 * a + i16, 4 * h + grp));
   };
+  // a stage whose activation rows follow its weight rows
+  auto read_ops = [&](const uint8_t* s, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) { read_ops2(s, s + TN * KB, h, wo, xo); };
   auto mma = [&](const u32x4(&wo)[WA], const u32x4(&xo)[4]) {
 #pragma unroll
     for (int a = 0; a < WA; ++a)
@@ -266,14 +268,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
   // Products of one whole LDS stage (the fp8 paths).  Native fp8: one k-step of
   // 128, 32 bytes per lane (k-chunks 2 grp, 2 grp + 1), weight operands taken
   // in two halves to bound the live registers.
-  auto compute = [&](const uint8_t* s) {
-    const uint8_t* w = s;
-    const uint8_t* x = s + TN * KB;
+  auto compute2 = [&](const uint8_t* w, const uint8_t* x) {
     if constexpr (!NATIVE8) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         u32x4 wo[WA], xo[4];
-        read_ops(s, h, wo, xo);
+        read_ops2(w, x, h, wo, xo);
         mma(wo, xo);
       }
     } else {
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       }
     }
   };
+  auto compute = [&](const uint8_t* s) { compute2(s, s + TN * KB); };
 
   // wait until at most n later stages' loads of this wave are outstanding
   auto wait_stages = [&](int n) {
@@ -358,14 +359,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       for (int i = 0; i < 16; ++i)
         lds_load16(aview, voff, (i < 8 ? run0 : run1) + (uint32_t)(i & 7) * blk_stride + koff, base + 1024 * i);
     };
-    // operands of k-step h of stage kt, as read_ops, from the two rings
+    // operands of k-step h of stage kt, from the two rings
     auto read_ring = [&](int kt, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) {
-      const uint8_t* w = wring + (kt % 3) * WBUF;
-      const uint8_t* x = xring + (kt % 2) * XBUF;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) xo[c] = *reinterpret_cast<const u32x4*>(x + swz<KB>(wm * 64 + 16 * c + i16, 4 * h + grp));
-#pragma unroll
-      for (int a = 0; a < WA; ++a) wo[a] = *reinterpret_cast<const u32x4*>(w + swz<KB>(wn * WN + 16 * a + i16, 4 * h + grp));
+      read_ops2(wring + (kt % 3) * WBUF, xring + (kt % 2) * XBUF, h, wo, xo);
     };
     if (!grp_b && nk > 0) {
       if (w_loader) {

@@ -184,6 +184,26 @@ def test_mfma_tile_height_invariance(H, cols, k_splits):
         assert torch.equal(part.cpu(), full[r:r + n]), (r, n)
 
 
+@pytest.mark.parametrize("family,cols,k_splits,silu", [(2, 512, 1, False), (2, 512, 1, True), (2, 128, 1, True),
+                                                     (2, 384, 1, False), (2, 1024, 2, False), (1, 512, 1, True),
+                                                     (1, 256, 2, False)])
+def test_mfma_fp8_tile_height_invariance(H, family, cols, k_splits, silu):
+    """fp8 weights on the matrix cores (native fp8 instruction: family 2; codes
+    decoded to bf16: family 1): a large batch runs on the 256-row activation
+    tile (the ring pipeline, and the L2 weight prefetch for stacked gate/up
+    matrices), a small one on the 128-row tile; a row's outputs are
+    bit-identical either way, down to K ranges of one 128-wide fp8 step."""
+    rows, n_all = 16384, 2048
+    W, s = make_w(rows, cols, wl.FP8, 21 + cols)
+    x = make_x(n_all, cols, wl.BF16, 22 + cols)
+    full, _ = run_proj(H, W, rows, cols, wl.FP8, s, family, x, wl.BF16, n_all, wl.BF16, silu=silu, k_splits=k_splits)
+    full = full.cpu()
+    for r, n in [(0, 3), (255, 2), (2045, 3), (600, 40), (1100, 129)]:
+        part, _ = run_proj(H, W, rows, cols, wl.FP8, s, family, x[r:r + n], wl.BF16, n, wl.BF16, silu=silu,
+                           k_splits=k_splits)
+        assert torch.equal(part.cpu(), full[r:r + n]), (r, n)
+
+
 @pytest.mark.parametrize("family,rows", [(0, 256), (0, 33000), (1, 256), (3, 256), (3, 70000)])
 def test_projection_batch_invariance(H, family, rows):
     """A row's outputs are bit-identical alone, in any batch size (the vector
