@@ -294,9 +294,10 @@ size_t pkd_attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t
  * merge.  On such chunked pools, in calls of at least 128 rows without
  * PKD_ROWS_DISTINCT_SEQS, runs of consecutive rows of one sequence at
  * consecutive positions (a prompt slice, [LRS] section 4, "Prefill: tensor
- * cores, written by hand") whose tile ends at position 1024 or later are read
- * as tiles of 2 x (16 / G) rows (16 / G for f32 pools), each K/V page once
- * per tile.
+ * cores, written by hand") are read as shared tiles: rows [t T, t T + T)
+ * with T the largest power of two (at most 64) for which T x G <= 64, when
+ * they are one such run and the tile ends at position 1024 or later.  A tile
+ * fetches each K/V page once, into LDS, for all its rows and query heads.
  */
 pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_heads,
                              const void* q, const void* k_new, const void* v_new,

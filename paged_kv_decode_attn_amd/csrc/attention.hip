@@ -244,6 +244,18 @@ __device__ __forceinline__ void mask_v(PageRegs<KVT, D>& vr, const bool (&valid)
   }
 }
 
+// Zeroes the V elements of the page's tokens past position plast.
+template <int KVT, int D>
+__device__ __forceinline__ void mask_v_past(PageRegs<KVT, D>& vr, int pg, int plast) {
+  bool valid[2][4];
+  const int t0 = pg * kPage + 4 * (lane_id() >> 4);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) valid[a][i] = t0 + 16 * a + i <= plast;
+  mask_v<KVT, D>(vr, valid);
+}
+
 // O^T += V^T . P^T for one page.  p[a][i] are the lane's softmax weights.
 template <int KVT, int D>
 __device__ __forceinline__ void page_pv(const PageRegs<KVT, D>& vr, const float (&p)[2][4],
@@ -299,18 +311,75 @@ __device__ __forceinline__ void page_pv(const PageRegs<KVT, D>& vr, const float 
 template <int KVT, int D>
 struct Acc {
   ORegs<KVT, D> O;
-  float m;  // running max (base-2 scaled scores) of head n
+  float m;  // reference maximum (base-2 scaled scores) of the lane's column, see page_weights
   float l;  // this lane's partial sum of weights
 };
 
 // 2^x by the hardware instruction: results below 2^-126 flush to zero, which
 // no softmax weight or rescale factor here can notice (the running sum is at
-// least 1).
+// least 1: the largest score is within kSlack above the reference).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// O *= alpha, skipped when no head's maximum moved (alpha == 1 in every lane:
-// the product would leave every bit as it is).  After the first pages the
-// running maximum seldom moves, so most pages skip the multiplies.
+// Online softmax with a lagging reference maximum.  Each column keeps m, the
+// reference its weights and sums are taken against, and moves it only when a
+// score exceeds it by more than kSlack (base-2 units; the first valid score
+// always sets it).  So weights lie in [0, 2^kSlack], and O and l are rescaled
+// on the rare pages where the reference moves instead of on every page whose
+// maximum grows; the result, O / l after the merge, is the same softmax.
+constexpr float kSlack = 8.0f;
+
+// Moves the reference m to cover the page maximum m_page when that exceeds it
+// by more than kSlack, and returns the factor for O and l (1 when it stays; 0
+// on the first valid page, where O and l are still zero).  A column with no
+// valid score so far keeps m = -inf and factor 1.
+__device__ __forceinline__ float next_reference(float& m, float m_page) {
+  const float cand = fmaxf(m, m_page);
+  const bool move = cand > m + kSlack;
+  const float alpha = move ? fast_exp2(m - cand) : 1.0f;
+  m = move ? cand : m;
+  return alpha;
+}
+
+// Weights of one page from its scores S (q . K): the token of score S at or
+// before position p_row gets p = 2^(s - m) with s = S qk_scale, and the
+// others 0 (MASK = false: the caller knows every token of the page is valid).
+// The empty asm keeps the compiler from fusing the scaling product into the
+// subtraction (a fused multiply-add would round once where this rounds twice,
+// and the token that sets the reference would not get weight exactly 1), so
+// both forms give the same bits wherever every token is valid, whatever the
+// kernel.  Updates the column's reference m and sum l, and returns the factor
+// by which the caller rescales O (rescale).
+template <bool MASK, int KVT, int D>
+__device__ __forceinline__ float page_weights(const AttnParams& P, Acc<KVT, D>& A, const f32x4_t (&S)[2], int pg,
+                                              int p_row, float (&p)[2][4]) {
+  const int t0 = pg * kPage + 4 * (lane_id() >> 4);
+  float s[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[a][i] = S[a][i] * P.qk_scale;
+      asm("" : "+v"(s[a][i]));
+      mx = fmaxf(mx, (!MASK || t0 + 16 * a + i <= p_row) ? s[a][i] : -INFINITY);
+    }
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  const float alpha = next_reference(A.m, mx);
+  float ls = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[a][i] = (!MASK || t0 + 16 * a + i <= p_row) ? fast_exp2(s[a][i] - A.m) : 0.f;
+      ls += p[a][i];
+    }
+  A.l = fmaf(A.l, alpha, ls);
+  return alpha;
+}
+
+// O *= alpha, skipped when no column's reference moved (alpha == 1 in every
+// lane: the product would leave every bit as it is).
 template <int KVT, int D>
 __device__ __forceinline__ void rescale(Acc<KVT, D>& A, float alpha) {
   using GE = Geo<KVT, D>;
@@ -319,78 +388,13 @@ __device__ __forceinline__ void rescale(Acc<KVT, D>& A, float alpha) {
   for (int mt = 0; mt < GE::NMT; ++mt) A.O[mt] *= alpha;
 }
 
-// Online-softmax update of one page from its scores; returns the weights p.
+// One page of a row's online softmax: weights p (masked on the row's last
+// page only) and the rescale of O.
 template <int KVT, int D>
 __device__ __forceinline__ void page_softmax(const AttnParams& P, Acc<KVT, D>& A, const f32x4_t (&S)[2], int pg,
-                                             int p_row, bool (&valid)[2][4], float (&p)[2][4]) {
-  using GE = Geo<KVT, D>;
-  const int grp = lane_id() >> 4;
-  float s[2][4];
-  float mx = -INFINITY;
-  const int t0 = pg * kPage + 4 * grp;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      valid[a][i] = t0 + 16 * a + i <= p_row;
-      s[a][i] = valid[a][i] ? S[a][i] * P.qk_scale : -INFINITY;
-      mx = fmaxf(mx, s[a][i]);
-    }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  const float m_new = fmaxf(A.m, mx);
-  const float alpha = fast_exp2(A.m - m_new);
-  float ls = 0.f;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[a][i] = fast_exp2(s[a][i] - m_new);
-      ls += p[a][i];
-    }
-  A.l = A.l * alpha + ls;
-  A.m = m_new;
-  rescale<KVT, D>(A, alpha);
-}
-
-// The same update when a column may have no valid token in the page, or in
-// any page so far (columns of a tile whose row ends earlier, or whose row has
-// no tokens in this chunk): a column with no valid token yet keeps m = -inf,
-// l = 0, O = 0, and a page without valid tokens leaves its state untouched.
-// Wherever page_softmax is defined (a valid token has been seen) both give the
-// same bits.
-template <int KVT, int D>
-__device__ __forceinline__ void page_softmax_masked(const AttnParams& P, Acc<KVT, D>& A, const f32x4_t (&S)[2],
-                                                    int pg, int p_row, float (&p)[2][4]) {
-  using GE = Geo<KVT, D>;
-  const int grp = lane_id() >> 4;
-  float s[2][4];
-  bool valid[2][4];
-  float mx = -INFINITY;
-  const int t0 = pg * kPage + 4 * grp;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      valid[a][i] = t0 + 16 * a + i <= p_row;
-      s[a][i] = valid[a][i] ? S[a][i] * P.qk_scale : -INFINITY;
-      mx = fmaxf(mx, s[a][i]);
-    }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  const float m_new = fmaxf(A.m, mx);
-  const bool any = m_new != -INFINITY;
-  const float alpha = any ? fast_exp2(A.m - m_new) : 1.0f;
-  float ls = 0.f;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[a][i] = valid[a][i] ? fast_exp2(s[a][i] - m_new) : 0.f;
-      ls += p[a][i];
-    }
-  A.l = A.l * alpha + ls;
-  A.m = m_new;
+                                             int p_row, float (&p)[2][4]) {
+  const float alpha = (pg + 1) * kPage <= p_row + 1 ? page_weights<false, KVT, D>(P, A, S, pg, p_row, p)
+                                                    : page_weights<true, KVT, D>(P, A, S, pg, p_row, p);
   rescale<KVT, D>(A, alpha);
 }
 
@@ -555,10 +559,9 @@ __device__ __forceinline__ bool run_unit(const AttnParams& P, Acc<KVT, D>& A, in
     page_scores<KVT, D>(kr, qv, qf, S);
     if (FUSE && pg + 1 == own) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (nxt) load(pg + 1, 0, kr);
-    bool valid[2][4];
     float p[2][4];
-    page_softmax<KVT, D>(P, A, S, pg, p_row, valid, p);
-    if ((pg + 1) * kPage > p_row + 1) mask_v<KVT, D>(vr, valid);  // partial last page
+    page_softmax<KVT, D>(P, A, S, pg, p_row, p);
+    if ((pg + 1) * kPage > p_row + 1) mask_v_past<KVT, D>(vr, pg, p_row);  // partial last page
     page_pv<KVT, D>(vr, p, A.O);
     if (nxt) load(pg + 1, 1, vr);
   }
@@ -613,23 +616,30 @@ __device__ __forceinline__ void zero_heads(const AttnParams& P, int r, int g) {
 // page reads are L2 hits, and a tile has T times fewer waves (measured: a
 // 256-row slice at positions 0..255 takes 49 us tiled and 37 us per row, one
 // at 1024..1279 takes 63 and 85).  Every kernel that schedules rows evaluates
-// this the same way: the per-row kernels leave such rows to attn_tile_kernel.
+// this the same way: the per-row kernels leave such rows to the tile workgroups (tile_unit).
+// Rows are checked one per lane, so the whole wave calls it.  A tile has at
+// most 64 rows, so its first position is positive.
 constexpr int kTileMinPos = 1024;
 
-__device__ __forceinline__ bool tile_shared(const AttnParams& P, int t) {
-  const int T = P.tile_rows, r0 = t * T, r1 = min(P.n_rows, r0 + T);
-  if (T <= 0 || r1 - r0 < 2) return false;
-  const int s0 = P.seq[r0], p0 = P.pos[r0];
-  if (p0 + (r1 - 1 - r0) < kTileMinPos) return false;
-  bool same = true;
-  for (int r = r0 + 1; r < r1; ++r) same = same && P.seq[r] == s0 && P.pos[r] == p0 + (r - r0);
-  return same;
+// Lane j reads row r0 + j of tile t (a tile has at most 64 rows); s0 and p0
+// return its first row's sequence and position.
+__device__ __forceinline__ bool tile_probe(const AttnParams& P, int t, int& s0, int& p0) {
+  const int T = P.tile_rows, r0 = t * T, nr = min(P.n_rows, r0 + T) - r0;
+  s0 = -1;
+  p0 = 0;
+  if (T <= 0 || nr < 2) return false;
+  const int j = lane_id();
+  const bool in = j < nr;
+  const int sj = in ? P.seq[r0 + j] : 0, pj = in ? P.pos[r0 + j] : 0;
+  s0 = __shfl(sj, 0, kWave);
+  p0 = __shfl(pj, 0, kWave);
+  if (p0 + nr - 1 < kTileMinPos) return false;
+  return __builtin_amdgcn_ballot_w64(in && (sj != s0 || pj != p0 + j)) == 0;
 }
 
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
-  return v;
+__device__ __forceinline__ bool tile_shared(const AttnParams& P, int t) {
+  int s0, p0;
+  return tile_probe(P, t, s0, p0);
 }
 
 // One wave per (row, kv head); every row is a single chunk.
@@ -719,7 +729,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   u32x4 qv[Geo<KVT, D>::NQ];
   float qf[Geo<KVT, D>::NQ];
   load_q<KVT, D>(P, r < P.n_rows ? r : 0, g, qv, qf);
-  // rows of a shared tile are attn_tile_kernel's: treated here as absent
+  // rows of a shared tile are tile_unit's: treated here as absent
   const bool in_range = r < P.n_rows && !(P.tile_rows > 0 && tile_shared(P, r / P.tile_rows));
   const int s = in_range ? P.seq[r] : -1, p = in_range ? P.pos[r] : 0;
   int count, tab;
@@ -763,10 +773,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 //   chunk (the one holding its own page) also appends the row's token, as in
 //   the direct kernel, and no other chunk reads that page.
 template <int KVT, int D, bool FUSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunked_kernel(AttnParams P) {
+__device__ __forceinline__ void chunked_unit(const AttnParams& P, int bx, int by) {
   using GE = Geo<KVT, D>;
   const int cw = (P.max_ch + 3) / 4;
-  const int r = blockIdx.x / cw, c = 4 * (blockIdx.x % cw) + (threadIdx.x >> 6), g = blockIdx.y;
+  const int r = bx / cw, c = 4 * (bx % cw) + (threadIdx.x >> 6), g = by;
   if (c >= P.max_ch) return;
   const int l = lane_id(), grp = l >> 4, n = l & 15;
   const int s = P.seq[r], p = P.pos[r];
@@ -774,16 +784,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // chunks past the row's context (most waves of a batch of short rows) leave
   // after this one load; chunk 0 stays to report a refused row
   if (c > 0 && c * P.chunk_pages >= npg) return;
+  // the shared-tile check, the row's count and the chunk's table window in
+  // one round trip (window lanes past the row's pages are never used)
+  const bool tiled = P.tile_rows > 0 && tile_shared(P, r / P.tile_rows);
+  const int count = seq_count(P, s);
+  const int pg0 = c * P.chunk_pages;
+  const bool s_ok = s >= 0 && s < P.max_seqs;
+  const int tab =
+      (s_ok && pg0 + l < min(P.max_pages, pg0 + P.chunk_pages)) ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
+  if (tiled) return;
   u32x4 qv[GE::NQ];
   float qf[GE::NQ];
   load_q<KVT, D>(P, r, g, qv, qf);
-  if (P.tile_rows > 0 && tile_shared(P, r / P.tile_rows)) return;
-  const int count = seq_count(P, s);
   if (!row_ok(P, s, p, count, c == 0 && g == 0)) return;
   const int nch = (npg + P.chunk_pages - 1) / P.chunk_pages;
   if (c >= nch) return;
-  const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
-  const int tab = pg0 + l < pg1 ? P.table[(int64_t)s * P.max_pages + pg0 + l] : 0;
+  const int pg1 = min(npg, pg0 + P.chunk_pages);
   Acc<KVT, D> A;
   const bool bad = (FUSE && c == nch - 1) ? run_unit<KVT, D, true>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf)
                                           : run_unit<KVT, D, false>(P, A, r, s, p, g, pg0, pg1, tab, qv, qf);
@@ -807,73 +823,125 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
 }
 
-// Shared tiles (prompt slices): one wave per (tile, page chunk, kv head).  The
-// 16 columns of each of the NB matrix-core blocks are (row, query head) pairs,
-// 16 / G rows per block, so each K and V page of the chunk is read once for the
-// whole tile instead of once per row.  Every column runs the per-row
-// arithmetic: the same pages in the same order, and the pages past its own
-// position are exact no-ops for it (no valid token: weights 0, rescale 1).  V
-// is masked past the tile's last position; the positions between a column's
-// own and the tile's last are tokens of this slice, all written before the
-// kernel runs.  So each row's output is bit-identical to the per-row kernels'.
+template <int KVT, int D, bool FUSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunked_kernel(AttnParams P) {
+  chunked_unit<KVT, D, FUSE>(P, blockIdx.x, blockIdx.y);
+}
+
+// Shared tiles (prompt slices): one workgroup of NW waves per (tile, page
+// chunk, kv head).  The tile's rows x G query heads are its columns, packed
+// densely: column j is (row j / G, query head j % G), and wave w holds columns
+// [16 NB w, 16 NB (w + 1)) as NB matrix-core blocks of 16 (a tile has at most
+// 16 NB NW columns).  The chunk's pages are fetched once per workgroup, straight
+// into an LDS ring of NBUF pages: each wave loads its share of every page, NBUF
+// - 1 pages ahead, and every wave reads each page from LDS in the byte layout
+// a global load would give.  Every column runs the per-row arithmetic: the
+// same pages in the same order, and the pages and tokens past its own position
+// are exact no-ops for it (no valid token: weights 0, rescale 1).  V is masked
+// past the tile's last position; the tokens between a column's own position
+// and the tile's last are tokens of this slice, all written before the kernel
+// runs.  So each row's output is bit-identical to the per-row kernels'.
 // Used with chunked pools only (the page chunks are what give a tile's pages
 // parallelism): a row with one chunk is finished here, the others leave
 // records for the ordered merge, and a refused row is reported here and
 // zeroed by the merge.
-template <int KVT, int D, int NB>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_tile_kernel(AttnParams P, int n_ch) {
-  using GE = Geo<KVT, D>;
-  const int t = blockIdx.x / n_ch, c = blockIdx.x % n_ch, g = blockIdx.y;
-  if (!tile_shared(P, t)) return;
-  const int l = lane_id(), grp = l >> 4, n = l & 15;
-  const int G = P.G, RPB = 16 / G;
-  const int r0 = t * P.tile_rows;
-  const int s = P.seq[r0];
-  const bool s_ok = s >= 0 && s < P.max_seqs;
-  const int count = seq_count(P, s);
-  int rw[NB], hh[NB], pc[NB], nch[NB];
-  bool live[NB], ok[NB];
-  int pmax = -1;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int j = b * RPB + n / G;
-    rw[b] = r0 + j;
-    live[b] = n < RPB * G && j < P.tile_rows && rw[b] < P.n_rows;
-    hh[b] = g * G + n % G;
-    pc[b] = live[b] ? P.pos[rw[b]] : -1;
-    ok[b] = live[b] && s_ok && pc[b] >= 0 && pc[b] < kPage * count;
-    nch[b] = ok[b] ? ((pc[b] + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages : 0;
-    if (ok[b]) pmax = max(pmax, pc[b]);
+constexpr int kTileWaves = 4;  // waves per tile workgroup
+
+template <int KVT, int D>
+struct TileCfg {
+  static constexpr int NW = kTileWaves;
+  static constexpr int NB = 1;                 // 16-column blocks per wave
+  static constexpr int COLS = 16 * NB * NW;    // columns of a tile
+  static constexpr int BLOCK = kPage * D * Geo<KVT, D>::ES;  // bytes of one K or V block
+  static constexpr int SLOT = 2 * BLOCK;                     // one page of one kv head: K block, V block
+  static constexpr int LOADS = 2 * Geo<KVT, D>::NL / NW;     // 1 KiB wave loads per page and wave
+  static constexpr int RING = 49152;                         // LDS bytes of the page ring (at least two pages)
+  static constexpr int NBUF = RING / SLOT < 2 ? 2 : RING / SLOT > 8 ? 8 : RING / SLOT;
+  static_assert(2 * Geo<KVT, D>::NL % NW == 0 && LOADS >= 1, "page loads must split evenly over the waves");
+  static_assert(NBUF >= 2 && LOADS * (NBUF - 2) <= 63, "ring deeper than the vmcnt counter");
+};
+
+// Waits until this wave's loads of all pages but the last `ahead` (< MAXA) it
+// issued have landed in LDS (vmcnt counts this wave's loads in issue order),
+// and until its own LDS reads are done.
+template <int LOADS, int MAXA>
+__device__ __forceinline__ void wait_pages(int ahead) {
+  if constexpr (MAXA <= 1) {
+    __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+    wait_lds_reads();
+  } else if (ahead >= MAXA - 1) {
+    __builtin_amdgcn_s_waitcnt(PKD_VMCNT(LOADS * (MAXA - 1)));
+    wait_lds_reads();
+  } else {
+    wait_pages<LOADS, MAXA - 1>(ahead);
   }
-  pmax = wave_max_i(pmax);
-  // refused rows: reported once (chunk 0, kv head 0), zeroed by the merge
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-    if (live[b] && !ok[b] && c == 0 && g == 0 && grp == 0 && n % G == 0)
-      atomicOr(P.err, !s_ok ? kErrSeq : kErrPos);
-  if (pmax < 0) return;
-  const int npg = (pmax + kPage) / kPage;
-  const int pg0 = c * P.chunk_pages, pg1 = min(npg, pg0 + P.chunk_pages);
-  if (pg0 >= npg) return;
-  bool act[NB];
-  int prow[NB];
+}
+
+// Workgroup bx of 8 ceil(units / 8) n_tiles, for units = chunks x kv heads.
+// Workgroup i runs on XCD i mod 8 (the tile workgroups come first in their
+// grid); the tiles of one (chunk, kv head) unit are given to one XCD, so that
+// its pages are fetched into one L2.
+template <int KVT, int D>
+__device__ __forceinline__ void tile_unit(const AttnParams& P, int bx, int n_tiles, int n_units) {
+  using GE = Geo<KVT, D>;
+  using TC = TileCfg<KVT, D>;
+  constexpr int NB = TC::NB;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[TC::NBUF * TC::SLOT];
+  const int xcd = bx % 8, y = bx / 8;
+  const int u = xcd + 8 * (y / n_tiles), t = y % n_tiles;
+  if (u >= n_units) return;
+  const int c = u / P.n_kv, g = u % P.n_kv;
+  const int wave = threadIdx.x >> 6, l = lane_id(), grp = l >> 4, n = l & 15;
+  const int G = P.G;
+  const int r0 = t * P.tile_rows, nr = min(P.n_rows, r0 + P.tile_rows) - r0;
+  // the queries depend on the tile's rows alone: requested before the rows
+  // are read, so that they arrive meanwhile (rows past the call are not read)
+  int jr[NB];
   u32x4 qv[NB][GE::NQ];
   float qf[NB][GE::NQ];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int j = (wave * NB + b) * 16 + n;
+    jr[b] = j / G;
+    const bool live = jr[b] < nr;
+    load_q_at<KVT, D>(P, live ? r0 + jr[b] : r0, live ? g * G + j % G : g * G, live, qv[b], qf[b]);
+  }
+  int s, p0;
+  if (!tile_probe(P, t, s, p0)) return;
+  const bool s_ok = s >= 0 && s < P.max_seqs;
+  // the sequence's count and the table window of this chunk, in one round trip
+  const int32_t* trow = P.table + (int64_t)(s_ok ? s : 0) * P.max_pages;
+  const int pg0 = c * P.chunk_pages;
+  const int count = seq_count(P, s);
+  int win = pg0;
+  int tab = (s_ok && pg0 + l < min(P.max_pages, pg0 + P.chunk_pages)) ? trow[pg0 + l] : 0;
+  // rows r0 + j are at positions p0 + j (p0 > 0, see tile_shared); the valid
+  // ones are a prefix, ending at the last position the table covers
+  const int plast = s_ok ? min(p0 + nr - 1, kPage * count - 1) : -1;
+  // refused rows: reported once (chunk 0, kv head 0), zeroed by the merge
+  if (plast < p0 + nr - 1 && c == 0 && g == 0 && threadIdx.x == 0) atomicOr(P.err, !s_ok ? kErrSeq : kErrPos);
+  if (plast < p0) return;
+  const int npg = (plast + kPage) / kPage;
+  const int pg1 = min(npg, pg0 + P.chunk_pages);
+  if (pg0 >= npg) return;
+  int rw[NB], hh[NB], prow[NB], nch[NB];
+  bool act[NB], on[NB];
   Acc<KVT, D> A[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    act[b] = ok[b] && c < nch[b];
-    prow[b] = act[b] ? pc[b] : -1;
-    load_q_at<KVT, D>(P, act[b] ? rw[b] : r0, hh[b], act[b], qv[b], qf[b]);
+    const int j = (wave * NB + b) * 16 + n;
+    const int pc = p0 + jr[b];
+    rw[b] = r0 + jr[b];
+    hh[b] = g * G + j % G;
+    nch[b] = (jr[b] < nr && pc <= plast) ? ((pc + kPage) / kPage + P.chunk_pages - 1) / P.chunk_pages : 0;
+    act[b] = c < nch[b];
+    prow[b] = act[b] ? pc : -1;
+    on[b] = __builtin_amdgcn_ballot_w64(act[b]) != 0;  // the block has work in this chunk
 #pragma unroll
     for (int mt = 0; mt < GE::NMT; ++mt) A[b].O[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     A[b].m = -INFINITY;
     A[b].l = 0.f;
   }
-  const int32_t* trow = P.table + (int64_t)s * P.max_pages;
-  const uint8_t* base = P.pages + (uint64_t)g * 2 * P.block_bytes;
-  int win = pg0;
-  int tab = pg0 + l < pg1 ? trow[pg0 + l] : 0;
   bool bad = refuse_window(P, pg1 - win, tab);
   auto page_of = [&](int pg) {
     if (pg - win >= kWave) {
@@ -883,35 +951,51 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     return __shfl(tab, pg - win, kWave);
   };
-  u32x4 kr[GE::NL], vr[GE::NL];
-  auto load = [&](int pg, int cc, PageRegs<KVT, D>& regs) {
-    load_block<KVT, D>(base + (uint64_t)page_of(pg) * P.page_stride + cc * P.block_bytes, regs);
+  const uint8_t* base = P.pages + (uint64_t)g * 2 * P.block_bytes;
+  // this wave's share of logical page pg (K block, then V block) into ring slot `slot`
+  auto issue = [&](int pg, int slot) {
+    const int page = __builtin_amdgcn_readfirstlane(page_of(pg));
+    const __amdgpu_buffer_rsrc_t v = operand_view(base + (uint64_t)page * P.page_stride, 2 * TC::BLOCK);
+#pragma unroll
+    for (int k = 0; k < TC::LOADS; ++k) {
+      const int q = wave + TC::NW * k;  // 1 KiB part q of the page's two blocks
+      lds_load16(v, (uint32_t)(1024 * q + 16 * l), 0, ring + slot * TC::SLOT + 1024 * q);
+    }
   };
-  load(pg0, 0, kr);
-  load(pg0, 1, vr);
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const bool nxt = pg + 1 < pg1;
+  const int np = pg1 - pg0;
+  for (int k = 0; k < TC::NBUF - 1 && k < np; ++k) issue(pg0 + k, k);
+  u32x4 kr[GE::NL], vr[GE::NL];
+  for (int i = 0; i < np; ++i) {
+    const int pg = pg0 + i;
+    // page i has landed for every wave, and every wave is done with page i - 1,
+    // whose slot the next request refills
+    wait_pages<TC::LOADS, TC::NBUF - 1>(min(np - 1 - i, TC::NBUF - 2));
+    lds_barrier();
+    if (i + TC::NBUF - 1 < np) issue(pg + TC::NBUF - 1, (i + TC::NBUF - 1) % TC::NBUF);
+    const lds_u8* kb = (const lds_u8*)ring + (i % TC::NBUF) * TC::SLOT;
+    load_block_lds<KVT, D>(kb, kr);
     f32x4_t S[NB][2];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) page_scores<KVT, D>(kr, qv[b], qf[b], S[b]);
-    if (nxt) load(pg + 1, 0, kr);
+    for (int b = 0; b < NB; ++b)
+      if (on[b]) page_scores<KVT, D>(kr, qv[b], qf[b], S[b]);
+    load_block_lds<KVT, D>(kb + TC::BLOCK, vr);
     float p[NB][2][4];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) page_softmax_masked<KVT, D>(P, A[b], S[b], pg, prow[b], p[b]);
-    if ((pg + 1) * kPage > pmax + 1) {
-      bool valid[2][4];
-      const int t0 = pg * kPage + 4 * grp;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) valid[a][i] = t0 + 16 * a + i <= pmax;
-      mask_v<KVT, D>(vr, valid);
+    for (int b = 0; b < NB; ++b) {
+      if (!on[b]) continue;
+      // every column of the block sees the whole page: the unmasked weights.
+      // O is rescaled in one place, after either form.
+      const float alpha = __builtin_amdgcn_ballot_w64(prow[b] < pg * kPage + kPage - 1) == 0
+                              ? page_weights<false, KVT, D>(P, A[b], S[b], pg, prow[b], p[b])
+                              : page_weights<true, KVT, D>(P, A[b], S[b], pg, prow[b], p[b]);
+      rescale<KVT, D>(A[b], alpha);
     }
+    if ((pg + 1) * kPage > plast + 1) mask_v_past<KVT, D>(vr, pg, plast);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) page_pv<KVT, D>(vr, p[b], A[b].O);
-    if (nxt) load(pg + 1, 1, vr);
+    for (int b = 0; b < NB; ++b)
+      if (on[b]) page_pv<KVT, D>(vr, p[b], A[b].O);
   }
-  if (bad && l == 0) atomicOr(P.err, kErrPage);
+  if (bad && threadIdx.x == 0) atomicOr(P.err, kErrPage);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     // a refused chunk leaves l = -1, which makes the merge zero the row
@@ -924,7 +1008,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
         store_out4<D>(P, rw[b], hh[b], 16 * mt + 4 * grp,
                       bad ? f32x4_t{0.f, 0.f, 0.f, 0.f} : A[b].O[mt] * inv * P.v_scale);
     } else {
-      const int64_t rec = rec_of(P, rw[b], c, g, n % G);
+      const int64_t rec = rec_of(P, rw[b], c, g, hh[b] - g * G);
       if (grp == 0) {
         P.part_ml[2 * rec] = A[b].m;
         P.part_ml[2 * rec + 1] = lsum;
@@ -933,6 +1017,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
       for (int mt = 0; mt < GE::NMT; ++mt)
         *reinterpret_cast<f32x4_t*>(P.part_o + rec * D + 16 * mt + 4 * grp) = A[b].O[mt];
     }
+  }
+}
+
+// Calls with shared tiles: the tile workgroups, then the per-row chunk
+// workgroups (chunk_x by kv heads of them, as attn_chunked_kernel's grid), in
+// one launch; the per-row workgroups of tiled rows leave after the tile check
+// while the tiles run.
+template <int KVT, int D>
+__global__ __launch_bounds__(64 * kTileWaves) __attribute__((amdgpu_waves_per_eu(3))) void attn_tiles_rows_kernel(
+    AttnParams P, int n_tile_wgs, int n_tiles, int n_units, int chunk_x) {
+  static_assert(kTileWaves == 4, "the per-row workgroups hold four waves");
+  if ((int)blockIdx.x < n_tile_wgs) {
+    tile_unit<KVT, D>(P, blockIdx.x, n_tiles, n_units);
+  } else {
+    const int i = blockIdx.x - n_tile_wgs;
+    chunked_unit<KVT, D, false>(P, i % chunk_x, i / chunk_x);
   }
 }
 
@@ -946,22 +1046,33 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
   const int hq = P.n_kv * P.G;
   const int r = blockIdx.x / hq, h = blockIdx.x % hq, g = h / P.G, n = h % P.G;
-  const int nch = row_chunks(P, P.seq[r], P.pos[r]);
-  if (nch == 1) return;
   const int l = lane_id();
   constexpr int PER = D / 64;  // dims per lane
+  // The records of the first chunks are requested before the row's chunk
+  // count is known (records past it hold stale values and are not used): lane
+  // c's (m, l) of chunk c < 64, and the O records of chunks 0..3.
+  float ms = -INFINITY, lsv = 0.f;
+  if (l < min(P.max_ch, kWave)) {
+    const int64_t rec = rec_of(P, r, l, g, n);
+    ms = P.part_ml[2 * rec];
+    lsv = P.part_ml[2 * rec + 1];
+  }
+  float v0[4][PER];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t rec = rec_of(P, r, min(u, P.max_ch - 1), g, n);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v0[u][j] = P.part_o[rec * D + PER * l + j];
+  }
+  const int nch = row_chunks(P, P.seq[r], P.pos[r]);
+  if (nch == 1) return;
   float o[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) o[j] = 0.f;
   if (nch > 0) {
     // lane c holds (m, l) of chunk c; chunks past the first 64 are read again
     // below, once the maximum is known
-    float m0 = -INFINITY, l0 = 0.f;
-    if (l < nch) {
-      const int64_t rec = rec_of(P, r, l, g, n);
-      m0 = P.part_ml[2 * rec];
-      l0 = P.part_ml[2 * rec + 1];
-    }
+    const float m0 = l < nch ? ms : -INFINITY, l0 = l < nch ? lsv : 0.f;
     float M = m0;
     // a chunk that met a table entry outside the pool left l = -1: the row is
     // refused and written as zeros
@@ -995,9 +1106,25 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
       // sums (a break there let the compiler wait for each record in turn);
       // records past cn are selected away, so every bit is that of adding
       // chunks c .. cn - 1 in order.
+      int c = 0;
+      if (c0 == 0) {  // chunks 0..3, from the records requested up front
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool in = u < cn;
+          const float w = __shfl(wl, min(u, cn - 1), kWave);
+          const float Ln = L + __shfl(ll, min(u, cn - 1), kWave) * w;
+          L = in ? Ln : L;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const float on = o[j] + v0[u][j] * w;
+            o[j] = in ? on : o[j];
+          }
+        }
+        c = 4;
+      }
       auto accumulate = [&](auto u_const) {
         constexpr int U = decltype(u_const)::value;
-        for (int c = 0; c < cn; c += U) {
+        for (; c < cn; c += U) {
           float v[U][PER];
 #pragma unroll
           for (int u = 0; u < U; ++u) {
@@ -1019,7 +1146,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
           }
         }
       };
-      if (cn <= 4) accumulate(std::integral_constant<int, 4>{});
+      if (cn - c <= 4) accumulate(std::integral_constant<int, 4>{});
       else accumulate(std::integral_constant<int, 16>{});
     }
     const float inv = nsum ? 1.0f / L : 0.0f;
@@ -1096,14 +1223,25 @@ size_t attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t max
   return carve(pool, n_q_heads, max_rows, nullptr, nullptr);
 }
 
-// Rows per shared tile: two 16-column blocks of 16 / G rows (one block for
-// f32 pools, whose page registers are twice as large).
-static int tile_rows_for(int kvt, int G) { return (kvt == PKD_F32 ? 1 : 2) * (16 / G); }
+// Rows per shared tile: the largest power of two whose rows x G query heads
+// fit the tile's columns (0: no tiles).  A power of two keeps a slice that
+// starts at an aligned row (after a batch of decode rows) on the tile grid.
+template <int KVT, int D>
+static int tile_rows_cfg(int G) {
+  int T = 0;
+  for (int t = 2; t * G <= TileCfg<KVT, D>::COLS && t <= kWave; t *= 2) T = t;
+  return T;
+}
+
+static int tile_rows_for(int kvt, int D, int G) {
+  if (D == 128) return kvt == PKD_F32 ? tile_rows_cfg<0, 128>(G) : kvt == PKD_BF16 ? tile_rows_cfg<1, 128>(G)
+                                                                                   : tile_rows_cfg<2, 128>(G);
+  return kvt == PKD_F32 ? tile_rows_cfg<0, 64>(G) : kvt == PKD_BF16 ? tile_rows_cfg<1, 64>(G) : tile_rows_cfg<2, 64>(G);
+}
 
 template <int KVT, int D>
 static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk, int n_ch,
                        bool stage, hipStream_t st) {
-  constexpr int NB = KVT == 0 ? 1 : 2;
   const int units = a.n_rows * n_kv;
   const dim3 tiles((a.n_rows + 3) / 4, n_kv);  // direct mode, staging: four rows of one kv head per workgroup
   const dim3 quads((units + 3) / 4);          // direct mode: four (row, kv head) units per workgroup
@@ -1125,9 +1263,13 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
     else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, false, false>), quads, dim3(256), 0, st, P);
     return;
   }
-  hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), chunk_grid, dim3(256), 0, st, P);
-  if (n_tiles)
-    hipLaunchKernelGGL((attn_tile_kernel<KVT, D, NB>), dim3(n_tiles * n_ch, n_kv), dim3(64), 0, st, P, n_ch);
+  if (n_tiles) {
+    const int n_units = n_ch * n_kv, n_tile_wgs = 8 * ((n_units + 7) / 8) * n_tiles;
+    hipLaunchKernelGGL((attn_tiles_rows_kernel<KVT, D>), dim3(n_tile_wgs + chunk_grid.x * n_kv), dim3(256), 0, st, P,
+                       n_tile_wgs, n_tiles, n_units, (int)chunk_grid.x);
+  } else {
+    hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), chunk_grid, dim3(256), 0, st, P);
+  }
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units * P.G), dim3(64), 0, st, P);
 }
 
@@ -1184,7 +1326,7 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   // one more launch and gives fewer waves).  A pure decode batch has no two
   // rows of one sequence.
   constexpr int kTileMinRows = 128;
-  P.tile_rows = (a.distinct || !ch || a.n_rows < kTileMinRows) ? 0 : tile_rows_for(kvt, P.G);
+  P.tile_rows = (a.distinct || !ch || a.n_rows < kTileMinRows) ? 0 : tile_rows_for(kvt, d.head_dim, P.G);
   // leading-page staging only where some page is listed by two sequences
   const bool stage = pool->shared_pages > 0;
   if (d.head_dim == 128) {

@@ -76,6 +76,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// ------------------------------------------------------------------ LDS staging
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+#define PKD_VMCNT(n) (0x0F70 | ((n) & 0xF) | (((n) & 0x30) << 10))
+
+// Raw buffer view of `bytes` bytes at `base`: loads past num_records bytes
+// (checked per dword, SGPR offset included) return zeros instead of touching
+// memory (the GEMM tiles that overhang the last weight or activation row are
+// filled this way).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_view(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte-per-lane load from a buffer view straight into LDS: lane l's
+// 16 bytes (at voff + soff) land at lds + 16 l (lds is wave-uniform).  The
+// host compilation pass never sees the device builtin.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, (int)soff, 0, 0);
+#else
+  (void)r;
+  (void)voff;
+  (void)soff;
+  (void)lds;
+#endif
+}
+
+// Workgroup barrier that no memory access may cross in either direction (the
+// compiler cannot see the LDS writes of the direct loads, so an intrinsic
+// barrier alone would let it hoist LDS reads above it).  It waits for nothing
+// by itself: the vmcnt / lgkmcnt waits around it are explicit.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // ------------------------------------------------------------------ sticky errors
 enum : unsigned { kErrSeq = 1u, kErrPos = 2u, kErrPage = 4u };
 

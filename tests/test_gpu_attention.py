@@ -414,12 +414,14 @@ def test_staging_variant_bit_identical(H, kvt, nq, nkv, d, append):
 
 
 PREFILL_CASES = [
-    # (kv dtype, q heads, kv heads, head dim, chunk pages): rows per shared tile = (1 or 2) x 16 / G
-    (wl.BF16, 4, 2, 128, 2),    # G 2: tiles of 16 rows
-    (wl.BF16, 28, 4, 128, 8),   # G 7: tiles of 4 rows
+    # (kv dtype, q heads, kv heads, head dim, chunk pages).  A tile has 128 columns
+    # (64 for f32 pools) of (row, query head) pairs: rows per tile = the largest
+    # power of two with rows x G within that
+    (wl.BF16, 4, 2, 128, 2),    # G 2: tiles of 64 rows
+    (wl.BF16, 28, 4, 128, 8),   # G 7: tiles of 16 rows (112 columns)
     (wl.FP8, 16, 8, 128, 3),    # G 2, fp8 pool
-    (wl.F32, 4, 2, 64, 2),      # f32 pool: one column block, tiles of 8 rows
-    (wl.BF16, 16, 1, 64, 5),    # G 16: tiles of 2 rows
+    (wl.F32, 4, 2, 64, 2),      # f32 pool: tiles of 32 rows
+    (wl.BF16, 16, 1, 64, 5),    # G 16: tiles of 8 rows
 ]
 
 
@@ -427,7 +429,7 @@ PREFILL_CASES = [
 def test_prefill_tiles_bit_identical(H, orc, kvt, nq, nkv, d, chunk):
     """A prompt slice (consecutive positions of one sequence) between decode
     rows of other sequences: its rows are read as shared tiles, each K/V page
-    once per tile.  Outputs are bit-identical to the per-row kernels (the same
+    fetched once per tile into LDS.  Outputs are bit-identical to the per-row kernels (the same
     rows afterwards, tiles off) and match the oracle; the slice starts and
     ends off the tile grid."""
     import paged_kv_decode_attn_amd as pkd
