@@ -296,8 +296,8 @@ size_t pkd_attn_workspace_bytes(const pkd_pool* pool, int32_t n_q_heads, int32_t
  * consecutive positions (a prompt slice, [LRS] section 4, "Prefill: tensor
  * cores, written by hand") are read as shared tiles: rows [t T, t T + T)
  * with T the largest power of two (at most 64) for which T x G <= 64, when
- * they are one such run and the tile ends at position 1024 or later.  A tile
- * fetches each K/V page once, into LDS, for all its rows and query heads.
+ * they are one such run.  A tile fetches each K/V page once, into LDS, for
+ * all its rows and query heads.
  */
 pkd_status paged_attn_decode(pkd_pool* pool, const pkd_rows* rows, int32_t n_q_heads,
                              const void* q, const void* k_new, const void* v_new,

@@ -363,16 +363,17 @@ __device__ __forceinline__ float page_weights(const AttnParams& P, Acc<KVT, D>& 
       asm("" : "+v"(s[a][i]));
       mx = fmaxf(mx, (!MASK || t0 + 16 * a + i <= p_row) ? s[a][i] : -INFINITY);
     }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
+  mx = max_xor16(mx);
+  mx = max_xor32(mx);
   const float alpha = next_reference(A.m, mx);
+  // the lane's sum starts at its first weight (no weight is -0)
   float ls = 0.f;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[a][i] = (!MASK || t0 + 16 * a + i <= p_row) ? fast_exp2(s[a][i] - A.m) : 0.f;
-      ls += p[a][i];
+      ls = (a == 0 && i == 0) ? p[a][i] : ls + p[a][i];
     }
   A.l = fmaf(A.l, alpha, ls);
   return alpha;
@@ -570,9 +571,7 @@ __device__ __forceinline__ bool run_unit(const AttnParams& P, Acc<KVT, D>& A, in
 
 // Sum of the lane-partial l over the four 16-lane groups (fixed butterfly).
 __device__ __forceinline__ float group_sum(float l) {
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-  return l;
+  return add_xor32(add_xor16(l));
 }
 
 template <int D>
@@ -610,16 +609,14 @@ __device__ __forceinline__ void zero_heads(const AttnParams& P, int r, int g) {
 }
 
 // Tiles for prompt slices: rows [t T, t T + T) (T = P.tile_rows) form a
-// shared tile when there are at least two of them, they are one sequence at
-// consecutive positions, and the last of them is at position kTileMinPos or
-// beyond.  Below that context the per-row kernels are faster: their redundant
-// page reads are L2 hits, and a tile has T times fewer waves (measured: a
-// 256-row slice at positions 0..255 takes 49 us tiled and 37 us per row, one
-// at 1024..1279 takes 63 and 85).  Every kernel that schedules rows evaluates
-// this the same way: the per-row kernels leave such rows to the tile workgroups (tile_unit).
-// Rows are checked one per lane, so the whole wave calls it.  A tile has at
-// most 64 rows, so its first position is positive.
-constexpr int kTileMinPos = 1024;
+// shared tile when there are at least two of them and they are one sequence
+// at consecutive positions from 0 up (a prompt slice).  Tiles were faster
+// than the per-row kernels at every measured context (256-row slices of a
+// 7B-shaped layer starting at positions 0, 256, 512, 768, 1024 and 2304:
+// 23, 28, 30, 32, 35 and 49 us tiled against 24, 33, 37, 42, 48 and 73 us per
+// row).  Every kernel that schedules rows evaluates this the same way: the
+// per-row kernels leave such rows to the tile workgroups (tile_unit).  Rows
+// are checked one per lane, so the whole wave calls it.
 
 // Lane j reads row r0 + j of tile t (a tile has at most 64 rows); s0 and p0
 // return its first row's sequence and position.
@@ -633,7 +630,7 @@ __device__ __forceinline__ bool tile_probe(const AttnParams& P, int t, int& s0, 
   const int sj = in ? P.seq[r0 + j] : 0, pj = in ? P.pos[r0 + j] : 0;
   s0 = __shfl(sj, 0, kWave);
   p0 = __shfl(pj, 0, kWave);
-  if (p0 + nr - 1 < kTileMinPos) return false;
+  if (p0 < 0) return false;  // the per-row kernels refuse such rows
   return __builtin_amdgcn_ballot_w64(in && (sj != s0 || pj != p0 + j)) == 0;
 }
 
@@ -915,8 +912,8 @@ __device__ __forceinline__ void tile_unit(const AttnParams& P, int bx, int n_til
   const int count = seq_count(P, s);
   int win = pg0;
   int tab = (s_ok && pg0 + l < min(P.max_pages, pg0 + P.chunk_pages)) ? trow[pg0 + l] : 0;
-  // rows r0 + j are at positions p0 + j (p0 > 0, see tile_shared); the valid
-  // ones are a prefix, ending at the last position the table covers
+  // rows r0 + j are at positions p0 + j (p0 >= 0, see tile_shared); the
+  // valid ones are a prefix, ending at the last position the table covers
   const int plast = s_ok ? min(p0 + nr - 1, kPage * count - 1) : -1;
   // refused rows: reported once (chunk 0, kv head 0), zeroed by the merge
   if (plast < p0 + nr - 1 && c == 0 && g == 0 && threadIdx.x == 0) atomicOr(P.err, !s_ok ? kErrSeq : kErrPos);
@@ -983,9 +980,11 @@ __device__ __forceinline__ void tile_unit(const AttnParams& P, int bx, int n_til
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (!on[b]) continue;
-      // every column of the block sees the whole page: the unmasked weights.
-      // O is rescaled in one place, after either form.
-      const float alpha = __builtin_amdgcn_ballot_w64(prow[b] < pg * kPage + kPage - 1) == 0
+      // every active column of the block sees the whole page: the unmasked
+      // weights (inactive columns are never stored; their queries are zero or
+      // real, so they stay finite).  O is rescaled in one place, after either
+      // form.
+      const float alpha = __builtin_amdgcn_ballot_w64(act[b] && prow[b] < pg * kPage + kPage - 1) == 0
                               ? page_weights<false, KVT, D>(P, A[b], S[b], pg, prow[b], p[b])
                               : page_weights<true, KVT, D>(P, A[b], S[b], pg, prow[b], p[b]);
       rescale<KVT, D>(A[b], alpha);
@@ -1319,12 +1318,11 @@ pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   const int kvt = d.kv_dtype;
   const int n_ch = ch ? (d.max_pages_per_seq + d.attn_chunk_pages - 1) / d.attn_chunk_pages : 1;
   P.max_ch = n_ch;
-  // Shared tiles pay only where page chunks give them parallelism (with one
-  // chunk per row a tile is a single wave walking every page, slower than one
-  // wave per row) and in calls of at least kTileMinRows rows (below that the
-  // per-row kernels were faster at every measured context: the tile kernel is
-  // one more launch and gives fewer waves).  A pure decode batch has no two
-  // rows of one sequence.
+  // Shared tiles run on chunked pools (the page chunks give a tile's pages
+  // parallelism, and the merge takes their records) in calls of at least
+  // kTileMinRows rows: below that they were no faster (16- to 64-row slices of
+  // a 7B-shaped layer: 2 us slower at position 1024, 3 us faster at 2304).  A
+  // pure decode batch has no two rows of one sequence.
   constexpr int kTileMinRows = 128;
   P.tile_rows = (a.distinct || !ch || a.n_rows < kTileMinRows) ? 0 : tile_rows_for(kvt, d.head_dim, P.G);
   // leading-page staging only where some page is listed by two sequences

@@ -63,6 +63,27 @@ __device__ __forceinline__ unsigned f32x2_to_fp8x2(float a, float b) {
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Exchanges across 16 and 32 lanes in registers (gfx950 lane swaps): with
+// both operands x, the two results hold x of this lane and of lane l ^ 16
+// (l ^ 32), in an order that depends on the lane, so a max or a sum of the
+// two equals the same operation on (x[l], x[l ^ d]) bit for bit.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Butterfly sum over the 64 lanes: every lane ends with the same value, formed by
 // the same fixed tree for every call (pairs at distance 32, 16, ..., 1).
 __device__ __forceinline__ float wave_sum(float v) {
