@@ -603,10 +603,15 @@ class Bench:
                                      reps, False)
             att_r, _, _ = self.timed(lambda: pkd.paged_attn_decode(poolp.handle, rows_row, nq, qa, None, None, oa, 1,
                                                                    wsa), reps, False)
+            # causal attention flops of the chunk: q.K and P.V over each row's context
+            att_flops = sum(4 * nq * d * (int(p) + 1) for p in wp.pos)
             res[f"pos{p0}"] = {
                 "us_chunk_step": round(us_chunk, 1), "tokens_per_s": round(nP / us_chunk * 1e6),
                 "us_token_by_token": round(us_tokens, 1), "speedup_vs_token_by_token": round(us_tokens / us_chunk, 1),
-                "attention_us_shared_tiles": round(att_t, 2), "attention_us_per_row": round(att_r, 2)}
+                "attention_us_shared_tiles": round(att_t, 2), "attention_us_per_row": round(att_r, 2),
+                "attention_gflop": round(att_flops / 1e9, 3),
+                "attention_tflops_shared_tiles": round(att_flops / att_t / 1e6, 1),
+                "attention_mfma_frac_shared_tiles": round(att_flops / att_t / 1e6 / MFMA_PEAK_TFLOPS["bf16"], 4)}
             del wp, poolp, layp, lay1
         return res
 
