@@ -555,7 +555,8 @@ class Bench:
         """Prefill of one 2,662-token prompt in 256-token chunks through the same
         layer shape: the chunk as one step (matrix-core projections, shared-tile
         attention) against the same 256 tokens one step each (vector GEMV at
-        batch 1), and the chunk's attention with shared tiles against per-row."""
+        batch 1), and the chunk's attention with shared tiles against per-row
+        (both replayed from graphs)."""
         import paged_kv_decode_attn_amd as pkd
         import workloads as wl
         import gpu_harness as H
@@ -598,11 +599,14 @@ class Bench:
             oa = torch.empty((nP, nq, d), dtype=torch.int16, device="cuda")
             wsa = H.aligned_empty(pkd.pkd_attn_workspace_bytes(poolp.handle, nq, nP))
             rows_row = pkd.make_rows(sp, pp, True)  # no append: the per-row kernels, tiles off
+            # the chunk's attention alone, replayed from a graph like the step (no host launch gaps)
             reps = max(self.args.steps, 10)
-            att_t, _, _ = self.timed(lambda: pkd.paged_attn_decode(poolp.handle, rows_p, nq, qa, None, None, oa, 1, wsa),
-                                     reps, False)
-            att_r, _, _ = self.timed(lambda: pkd.paged_attn_decode(poolp.handle, rows_row, nq, qa, None, None, oa, 1,
-                                                                   wsa), reps, False)
+            att_t, _, _, _ = self.graph_steps(
+                lambda st: pkd.paged_attn_decode(poolp.handle, rows_p, nq, qa, None, None, oa, 1, wsa, stream=st),
+                reps, 3)
+            att_r, _, _, _ = self.graph_steps(
+                lambda st: pkd.paged_attn_decode(poolp.handle, rows_row, nq, qa, None, None, oa, 1, wsa, stream=st),
+                reps, 3)
             # causal attention flops of the chunk: q.K and P.V over each row's context
             att_flops = sum(4 * nq * d * (int(p) + 1) for p in wp.pos)
             res[f"pos{p0}"] = {
