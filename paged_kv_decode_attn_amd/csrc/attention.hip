@@ -1041,7 +1041,11 @@ __global__ __launch_bounds__(64 * kTileWaves) __attribute__((amdgpu_waves_per_eu
 // reduction and the weights are computed in parallel; the weighted sums of l
 // and of O are then taken in ascending chunk order, with the O loads of
 // several chunks in flight at once.
-template <int D>
+// UMAX: the largest number of chunk records requested at a time past the
+// first four (4 or 16; the same sums either way).  16 serves pools whose rows
+// can have many chunks; 4 keeps the kernel at 48 VGPRs, so that every wave of
+// a large merge is resident at once.
+template <int D, int UMAX>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
   const int hq = P.n_kv * P.G;
   const int r = blockIdx.x / hq, h = blockIdx.x % hq, g = h / P.G, n = h % P.G;
@@ -1145,8 +1149,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnParams P) {
           }
         }
       };
-      if (cn - c <= 4) accumulate(std::integral_constant<int, 4>{});
-      else accumulate(std::integral_constant<int, 16>{});
+      if (UMAX == 4 || cn - c <= 4) accumulate(std::integral_constant<int, 4>{});
+      else accumulate(std::integral_constant<int, UMAX>{});
     }
     const float inv = nsum ? 1.0f / L : 0.0f;
 #pragma unroll
@@ -1238,6 +1242,14 @@ static int tile_rows_for(int kvt, int D, int G) {
   return kvt == PKD_F32 ? tile_rows_cfg<0, 64>(G) : kvt == PKD_BF16 ? tile_rows_cfg<1, 64>(G) : tile_rows_cfg<2, 64>(G);
 }
 
+// The ordered merge, one wave per (row, query head): records requested 16 at a
+// time on pools whose rows may have more than 12 chunks, 4 otherwise.
+template <int D>
+static void launch_merge(const AttnParams& P, int waves, hipStream_t st) {
+  if (P.max_ch > 12) hipLaunchKernelGGL((attn_merge_kernel<D, 16>), dim3(waves), dim3(64), 0, st, P);
+  else hipLaunchKernelGGL((attn_merge_kernel<D, 4>), dim3(waves), dim3(64), 0, st, P);
+}
+
 template <int KVT, int D>
 static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, int n_kv, bool chunk, int n_ch,
                        bool stage, hipStream_t st) {
@@ -1252,7 +1264,7 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
   const dim3 chunk_grid(a.n_rows * ((n_ch + 3) / 4), n_kv);
   if (chunk && a.k_new && a.distinct) {
     hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, true>), chunk_grid, dim3(256), 0, st, P);
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units * P.G), dim3(64), 0, st, P);
+    launch_merge<D>(P, units * P.G, st);
     return;
   }
   if (a.k_new) hipLaunchKernelGGL((append_kernel<KVT, D>), dim3(units), dim3(64), 0, st, P);
@@ -1269,7 +1281,7 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
   } else {
     hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), chunk_grid, dim3(256), 0, st, P);
   }
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(units * P.G), dim3(64), 0, st, P);
+  launch_merge<D>(P, units * P.G, st);
 }
 
 pkd_status attn_launch(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream, pkd_error* err) {
