@@ -610,3 +610,61 @@ def test_prefill_tiles_randomized(H, orc, i, kvt, d, nkv, G, chunk, p0, n_slice,
     assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
     want = oracle_attn(orc, w, seq, pos, q, kn, vn)
     assert H.rel_err(out.numpy(), want) <= TOL_F32_OUT
+
+
+def _decode_codes(codes: torch.Tensor, kvt: int, scale: float) -> torch.Tensor:
+    if kvt == wl.F32:
+        return codes.float()
+    if kvt == wl.BF16:
+        return codes.view(torch.bfloat16).float()
+    return codes.view(torch.float8_e4m3fn).float() * scale
+
+
+@pytest.mark.parametrize("kvt,chunk", [(wl.BF16, 2), (wl.BF16, 100), (wl.FP8, 3), (wl.F32, 5)])
+def test_reference_moves_mid_row(H, orc, kvt, chunk):
+    """Keys planted in later pages score far above every earlier key (base-2
+    jumps of about 14, 28, 56 and 112, against the softmax reference's slack
+    of 8), so the reference moves and O and l are rescaled in the middle of a
+    row, which random keys almost never make happen.  Per-row kernels and
+    shared tiles against the oracle, tiles bit-identical to the per-row
+    kernels (chunk 100 leaves the pool unchunked: the direct kernel)."""
+    import paged_kv_decode_attn_amd as pkd
+    nq, nkv, d = 8, 2, 128
+    lens = (1300, 300, 700)
+    w = wl.make("attn", "cpu", seed=31, n_q=nq, n_kv=nkv, d=d, kv_dtype=kvt, lens=lens, append=False,
+                chunk=chunk, extra_pages=0)
+    gen = torch.Generator().manual_seed(32)
+    c = torch.randn(d, generator=gen)
+    c = c / c.norm()
+    qd = wl.F32 if kvt == wl.F32 else wl.BF16
+
+    def queries(n):  # every query leans on c (q . c ~ 11 +- 1), so keys along c score high for all
+        return wl.encode(torch.randn((n, nq, d), generator=gen) + 11.0 * c, qd)
+
+    hk = _decode_codes(w.hist_k, kvt, w.k_scale).clone()
+    for s, L in enumerate(w.hist_len):
+        o = int(w.hist_off[s])
+        for t, beta in ((100, 10.0), (260, 20.0), (650, 40.0), (1210, 80.0)):
+            if t < L:
+                hk[o + t] = beta * c
+    ks = wl.fp8_scale(hk) if kvt == wl.FP8 else 1.0
+    w.hist_k = wl.encode(hk, kvt, ks)
+    w.k_scale = ks
+    w.q = queries(len(lens))
+    pool = H.GpuPool(w)
+    out = H.run_attention(pool, w.seq, w.pos, w.q.cuda(), None, None, distinct=True).cpu()
+    e = H.rel_err(out.numpy(), oracle_attn(orc, w, w.seq, w.pos, w.q))
+    print(f"reference moves, kv{kvt} chunk {chunk}: per row {e:.2e}", flush=True)
+    assert e <= TOL_F32_OUT
+    # a 200-row prompt slice of sequence 0 at positions 1000..1199
+    n = 200
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(1000, 1000 + n, dtype=np.int32)
+    q2 = queries(n)
+    tiled = H.run_attention(pool, seq, pos, q2.cuda(), None, None).cpu()
+    per_row = H.run_attention(pool, seq, pos, q2.cuda(), None, None, distinct=True).cpu()
+    assert torch.equal(tiled.view(torch.int32), per_row.view(torch.int32))
+    e2 = H.rel_err(tiled.numpy(), oracle_attn(orc, w, seq, pos, q2))
+    print(f"  slice {e2:.2e}", flush=True)
+    assert e2 <= TOL_F32_OUT
+    pkd.pkd_pool_check(pool.handle)
