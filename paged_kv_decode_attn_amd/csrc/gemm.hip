@@ -96,12 +96,19 @@ struct Tile {
 };
 
 // Byte offset of 16-byte chunk `chunk` of LDS row `row` (rows of KB bytes).
-// The XOR spreads the 16 rows that one matrix-core operand read touches over
-// all 64 banks: 128-byte rows use row & 7, 64-byte rows (four per 256 bytes)
-// use (row >> 2) & 3.
-template <int KB>
+// The XOR spreads the rows that one matrix-core operand read touches over the
+// 64 banks: 128-byte rows use row & 7, 64-byte rows (four per 256 bytes) use
+// (row >> 2) & 3.  Measured on the card (SQ_LDS_BANK_CONFLICT), a 16-byte
+// read serves lanes {0-7, 16-23}, {8-15, 24-31}, {32-39, 48-55} and {40-47,
+// 56-63} together.  The bf16 operand reads (lane group g at chunk c + g) are
+// conflict-free with row & 7; the native fp8 reads (group g at chunks 2g and
+// 2g + 1) were 2-way conflicted with it and are conflict-free with F8: rows
+// r and chunks two apart then never share a bank group (the XOR values of
+// the four rows of one parity are {0, 1, 4, 5}).
+template <int KB, bool F8 = false>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (KB == 128) return row * 128 + ((chunk ^ (row & 7)) << 4);
+  if constexpr (KB == 128 && F8) return row * 128 + ((chunk ^ ((row & 4) | ((row >> 1) & 1))) << 4);
+  else if constexpr (KB == 128) return row * 128 + ((chunk ^ (row & 7)) << 4);
   else return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
@@ -135,9 +142,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
   // contiguous items [x base + min(x, rem), ...), one extra for x < rem
   const int base8 = items / 8, rem8 = items % 8, xcd = b % 8;
   const int item = xcd * base8 + min(xcd, rem8) + b / 8;
-  const int tm = item % P.tiles_m;
-  const int sp = (item / P.tiles_m) % P.splits;
-  const int tn = item / (P.tiles_m * P.splits);
+  // items in order: groups of g weight units u = tn S + sp (the last group
+  // possibly shorter), each group's tiles with the unit varying fastest, so
+  // that with 8 or more activation tiles the 32 workgroups an XCD runs at once
+  // are 4 weight units x 8 activation tiles (12 operand streams, not 18)
+  const int units = P.tiles_n * P.splits, g = P.tiles_m >= 8 ? 4 : 1;
+  const int grp_i = item / (g * P.tiles_m), r = item % (g * P.tiles_m);
+  const int u0 = grp_i * g, gs = min(g, units - u0);
+  const int tm = r / gs, u = u0 + r % gs;
+  const int sp = u % P.splits;
+  const int tn = u / P.splits;
   const int n0 = tn * TN, m0 = tm * TM;
   const int t = threadIdx.x, wave = t >> 6, l = t & 63, grp = l >> 4, i16 = l & 15;
   const int wn = wave / T::MW, wm = wave % T::MW;  // weight slab of WN rows, activation slab of 64 rows
@@ -157,7 +171,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
   constexpr int CPR = KB / 16;  // 16-byte chunks per LDS row
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int lrow = l / CPR, lch = l % CPR;
-  const int gch = KB == 128 ? (lch ^ (lrow & 7)) : (lch ^ ((lrow >> 2) & 3));
+  const int gch = KB != 128 ? (lch ^ ((lrow >> 2) & 3)) : NATIVE8 ? (lch ^ ((lrow & 4) | ((lrow >> 1) & 1))) : (lch ^ (lrow & 7));
   const uint32_t voff = (uint32_t)(lrow * kbytes + 16 * gch);
   const __amdgpu_buffer_rsrc_t wview = operand_view(P.W, (uint32_t)(P.N * kbytes));
   const __amdgpu_buffer_rsrc_t xview = operand_view(P.X, (uint32_t)(P.M * kbytes));
@@ -249,8 +263,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int row = wm * 64 + 16 * c + i16;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(x + swz<KB>(row, 2 * grp));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(x + swz<KB>(row, 2 * grp + 1));
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(x + swz<KB, true>(row, 2 * grp));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(x + swz<KB, true>(row, 2 * grp + 1));
         xo[c] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
@@ -259,8 +273,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
         for (int a = 0; a < WA / 2; ++a) {
           const int row = wn * WN + 16 * (h * WA / 2 + a) + i16;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(w + swz<KB>(row, 2 * grp));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(w + swz<KB>(row, 2 * grp + 1));
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(w + swz<KB, true>(row, 2 * grp));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(w + swz<KB, true>(row, 2 * grp + 1));
           wo[a] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
 #pragma unroll
