@@ -184,6 +184,36 @@ def test_mfma_tile_height_invariance(H, cols, k_splits):
         assert torch.equal(part.cpu(), full[r:r + n]), (r, n)
 
 
+@pytest.mark.parametrize("family,wdt,k_splits", [(1, wl.BF16, 1), (1, wl.BF16, 3), (2, wl.FP8, 1), (2, wl.FP8, 3)])
+def test_mfma_tile_windows_cover_every_tile(H, family, wdt, k_splits):
+    """With 8 or more activation tiles the matrix-core tiles run in windows
+    of 4 weight units (weight tile x K split) x the activation tiles, the last
+    window group shorter when the unit count is not a multiple of 4 (5 weight
+    tiles: groups of 4 + 1 units, or 4 + 4 + 4 + 3 with 3 splits).  Every
+    output is written (the output starts as NaN) and equals, bit for bit, the
+    same rows run in 256-row launches (fewer than 8 activation tiles: the
+    plain order)."""
+    import paged_kv_decode_attn_amd as pkd
+    rows, cols, n_all = 1280, 512, 2048
+    W, s = make_w(rows, cols, wdt, 31 + k_splits)
+    x = make_x(n_all, cols, wl.BF16, 32)
+    M = pkd.make_matrix(W.cuda(), rows, cols, wdt, s, family, k_splits)
+    xd = x.cuda()
+
+    def run(r0, n):
+        y = torch.full((n, rows), float("nan"), dtype=torch.float32, device="cuda")
+        wsb = pkd.pkd_gemv_workspace_bytes(M, n)
+        ws = H.aligned_empty(wsb) if wsb else None
+        pkd.gemv_rows(M, xd[r0:r0 + n], wl.BF16, n, y, wl.F32, None, False, None, ws)
+        torch.cuda.synchronize()
+        return y.cpu()
+
+    full = run(0, n_all)
+    assert not torch.isnan(full).any()
+    for r0 in range(0, n_all, 256):
+        assert torch.equal(run(r0, 256), full[r0:r0 + 256]), r0
+
+
 @pytest.mark.parametrize("family,cols,k_splits,silu", [(2, 512, 1, False), (2, 512, 1, True), (2, 128, 1, True),
                                                      (2, 384, 1, False), (2, 1024, 2, False), (1, 512, 1, True),
                                                      (1, 256, 2, False)])
