@@ -303,113 +303,107 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     // Two groups of four waves (A = waves 0..3, B = waves 4..7; one of each
     // per SIMD) run half a stage apart: while one wave of a SIMD issues the 64
     // products of a stage back to back, the other reads its operands of the
-    // next stage from LDS, and at each barrier they swap.  B starts one
-    // barrier late; every barrier is shared by both groups.
+    // stage from LDS, and at each barrier they swap.  B starts one barrier
+    // late; every barrier is shared by both groups.
     //   A: M0 | C0 | M1 | C1 ...      B: - | M0 | C0 | M1 ...
-    // M(t) reads stage t (buffer t % 2) into registers; C(t) runs its products.
-    // Only A loads stages: stage t + 1 at the start of A's M(t) (stages 0, 1
-    // before the loop), into the buffer of stage t - 1, which both groups
-    // finished reading before A's M(t) began; A waits for it at the end of its
-    // C(t), so the barrier that opens M(t + 1) publishes it.
-    // The weight half of stage t sits in weight buffer t % 3 and the
-    // activation half in activation buffer t % 2.  Waves 0, 1 load weights,
-    // waves 2, 3 activations: at the start of A's M(t), stage t + 2's weights
-    // and stage t + 1's activations, each into the buffer of stage t - 1,
-    // which both groups finished reading before A's M(t) began.  So the
-    // weights (the operand that misses L2: each block is read by the few row
-    // tiles that share it) have four phases to land, the activations two.  A
-    // wave waits at the end of its C(t) for its part of stage t + 1 only.
+    // M(t) reads stage t into registers; C(t) runs its products.  The weight
+    // half of stage t sits in weight buffer t % 3, the activation half in
+    // activation buffer t % 2 (3 x 32 + 2 x 32 KiB = 160 KiB).
+    // Each wave loads one 64-row quarter of one operand (8 wave loads per
+    // stage), at the start of its M phase: A waves the activations of stage
+    // t + 1 at M(t), B waves the weights of stage t + 2 at their M(t), each
+    // into the buffer of stage t - 1, which both groups finished reading
+    // before.  A wave's M phase then issues 8 loads besides its 24 LDS reads,
+    // about as long as the other group's products (issuing all 16 loads of a
+    // wave in one M phase made that phase the longer one: measured 1,550-1,650
+    // clocks against 1,160 for the products).  Activations have two phases to
+    // land (A waits at the end of its C(t)); weights, the operand that misses
+    // L2, three (B waits for stage t + 1's at the end of its M(t)).
     static_assert(STAGES == 2 && DPW == 8 && T::WRING, "weight ring of three, activation ring of two");
     const bool grp_b = wave_u >= 4;
-    const bool w_loader = wave_u < 2;
+    const bool w_loader = grp_b;
+    const int quarter = wave_u & 3;
     u32x4 wo0[WA], xo0[4], wo1[WA], xo1[4];
     constexpr int WBUF = TN * KB, XBUF = TM * KB;
     uint8_t* const wring = smem;
     uint8_t* const xring = smem + 3 * WBUF;
-    // An A wave w fills LDS rows 128 (w % 2) .. + 127 of the weight part (w < 2)
-    // or of the activation part (w = 2, 3): two runs of 64 consecutive global
-    // rows (gate and up halves of a slab under silu), each starting at a
-    // wave-uniform row.
-    const uint32_t run0 = (uint32_t)block_row(16 * (wave_u & 3)) * (uint32_t)kbytes;
-    const uint32_t run1 = (uint32_t)block_row(16 * (wave_u & 3) + 8) * (uint32_t)kbytes;
+    // A wave's quarter is LDS rows 64 q .. 64 q + 63 of its operand: one run of
+    // 64 consecutive global rows (under silu, 64 gate or 64 up rows of a slab)
+    // starting at a wave-uniform row.
+    const uint32_t run = (uint32_t)block_row(w_loader ? 8 * quarter : TN / RPB + 8 * quarter) * (uint32_t)kbytes;
     const uint32_t blk_stride = 8 * (uint32_t)kbytes;
     const __amdgpu_buffer_rsrc_t aview = w_loader ? wview : xview;
-    auto dma_a = [&](int kt) {
-      uint8_t* base = (w_loader ? wring + (kt % 3) * WBUF : xring + (kt % 2) * XBUF) + 16 * 1024 * (wave_u & 1);
+    auto dma_q = [&](int kt) {
+      uint8_t* base = (w_loader ? wring + (kt % 3) * WBUF : xring + (kt % 2) * XBUF) + 8 * 1024 * quarter;
       const uint32_t koff = (uint32_t)(kt0 + kt) * KT_BYTES;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        lds_load16(aview, voff, (i < 8 ? run0 : run1) + (uint32_t)(i & 7) * blk_stride + koff, base + 1024 * i);
+      for (int i = 0; i < 8; ++i) lds_load16(aview, voff, run + (uint32_t)i * blk_stride + koff, base + 1024 * i);
     };
     // operands of k-step h of stage kt, from the two rings
     auto read_ring = [&](int kt, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) {
       read_ops2(wring + (kt % 3) * WBUF, xring + (kt % 2) * XBUF, h, wo, xo);
     };
-    if (!grp_b && nk > 0) {
-      if (w_loader) {
-        dma_a(0);
-        if (nk > 1) {
-          dma_a(1);
-          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
-        } else {
-          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
-        }
+    if (nk > 0) {
+      dma_q(0);
+      if (w_loader && nk > 1) {
+        dma_q(1);
+        __builtin_amdgcn_s_waitcnt(PKD_VMCNT(8));
       } else {
-        dma_a(0);
         __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
       }
     }
     lds_barrier();
     if (grp_b) lds_barrier();
     // Stacked gate/up matrices: the weight loaders also request the weight
-    // lines of stage t + PF into L2 (one dword per lane and row run), so that
-    // stage's loads into LDS find them there.  The values are folded into
-    // pf_acc, read once the wait below has retired them, and consumed after
+    // lines of stage t + PF into L2 (one dword per lane of their 64-row run),
+    // so that stage's loads into LDS find them there.  The values are folded
+    // into pf_acc, read once a later wait has retired them, and consumed after
     // the loop under a condition that never holds.  Measured: gate/up 3-9%
     // faster at batches 256 to 4,096; on the down and qkv shapes the same
     // prefetch cost 3-4%, so it is used for silu-pair matrices only.
     constexpr int PF = 6;
-    unsigned pf_acc = 0, pf_prev0 = 0, pf_prev1 = 0;
+    unsigned pf_acc = 0, pf_prev = 0;
     for (int kt = 0; kt < nk; ++kt) {
       // M(kt)
       const int ahead = w_loader ? kt + 2 : kt + 1;
-      const bool issued = !grp_b && ahead < nk;
-      if (issued) dma_a(ahead);
-      const bool pf = w_loader && !grp_b && P.silu && kt + PF < nk;
-      unsigned pf0 = 0, pf1 = 0;
+      const bool issued = ahead < nk;
+      if (issued) dma_q(ahead);
+      const bool pf = w_loader && P.silu && kt + PF < nk;
+      unsigned pf0 = 0;
       if (pf) {
         const uint32_t koffp = (uint32_t)(kt0 + kt + PF) * KT_BYTES;
-        pf0 = __builtin_amdgcn_raw_buffer_load_b32(wview, (uint32_t)(l * kbytes), run0 + koffp, 0);
-        pf1 = __builtin_amdgcn_raw_buffer_load_b32(wview, (uint32_t)(l * kbytes), run1 + koffp, 0);
+        pf0 = __builtin_amdgcn_raw_buffer_load_b32(wview, (uint32_t)(l * kbytes), run + koffp, 0);
       }
       read_ring(kt, 0, wo0, xo0);
       read_ring(kt, 1, wo1, xo1);
       wait_lds_reads();
+      // B: the weights of stage kt + 1 have landed (stage kt + 2's 8 loads
+      // and this stage's prefetch may still be in flight)
+      if (w_loader) {
+        if (issued) {
+          if (pf) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(9));
+          else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(8));
+        } else {
+          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+        }
+      }
+      pf_acc ^= pf_prev;
+      pf_prev = pf0;
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // C(kt)
       mma(wo0, xo0);
       mma(wo1, xo1);
-      // this wave's part of stage kt + 1 has landed (a weight loader may still
-      // have stage kt + 2's 16 loads and this stage's 2 prefetches in flight)
-      if (!grp_b) {
-        if (w_loader && issued) {
-          if (pf) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(18));
-          else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(16));
-        } else {
-          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
-        }
-      }
-      pf_acc ^= pf_prev0 ^ pf_prev1;
-      pf_prev0 = pf0;
-      pf_prev1 = pf1;
+      // A: the activations of stage kt + 1 have landed
+      if (!w_loader) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!grp_b) lds_barrier();
-    pf_acc ^= pf_prev0 ^ pf_prev1;
+    __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
+    pf_acc ^= pf_prev;
     if (pf_acc == 0x9e3779b9u && P.M < 0) reinterpret_cast<float*>(P.y)[0] = 0.f;
   } else if constexpr (MODE == 0) {
     // Ping-pong over the KS = KB / 64 k-steps of each stage: the operands of
