@@ -11,11 +11,12 @@
 // Workgroup tile: TN = 256 weight rows x TM = 128 or 256 activation rows, k-tile
 // of 128 bytes per row, eight waves (two per SIMD, so that one wave's LDS and
 // memory waits overlap the other's products).  TM = 256: waves of 128 x 64
-// (8 x 4 matrix-core tiles of 16 x 16), two LDS stages of 64 KiB; TM = 128:
-// waves of 64 x 64, three stages of 48 KiB.  The taller tile halves the bytes
-// each CU pulls from L2 per product; the shorter one keeps small batches busy.
-// LDS rows hold 128 bytes with an XOR swizzle of the 16-byte chunks (row r,
-// chunk c at c ^ (r & 7)), so the operand reads of a wave hit distinct banks.
+// (8 x 4 matrix-core tiles of 16 x 16); bf16 stages in a ring of three 32 KiB
+// weight and two 32 KiB activation buffers, native fp8 in two stages of 64
+// KiB; TM = 128: waves of 64 x 64, three stages of 48 KiB.  The taller tile
+// halves the bytes each CU pulls from L2 per product; the shorter one keeps
+// small batches busy.  LDS rows hold 128 bytes with an XOR swizzle of the
+// 16-byte chunks (swz), so the operand reads of a wave hit distinct banks.
 //   mode 0 (bf16) and mode 2 (native fp8): stages fed by buffer loads that
 //     write LDS directly (buffer_load_dwordx4 ... lds), waited on explicitly;
 //   mode 1 (fp8 decoded to bf16): the codes pass through registers, are widened
@@ -24,7 +25,8 @@
 // its tile.  With k_splits S > 1 each tile's K range is cut into S fixed parts
 // whose fp32 partial sums a second kernel adds in ascending order, so results
 // depend on S (a per-matrix constant) but never on the batch.  Work items are
-// dealt so that an XCD runs a contiguous run of tiles sharing a weight block.
+// dealt so that an XCD runs a contiguous run of tiles sharing weight blocks
+// (in windows of 4 weight units x 8 activation tiles when there are 8 or more).
 
 #include <atomic>
 
