@@ -84,11 +84,10 @@ struct Tile {
   static constexpr int KB = 128;
   static constexpr int STAGE_BYTES = (TN + TM) * KB;
   static constexpr int STAGES = MODE == 1 ? 2 : (TM == 256 ? 2 : 3);
-  // bf16, TM = 256: the weight part of a stage has three buffers and the
-  // activation part two (the weights are requested two stages ahead), 160 KiB.
-  // (The same ring on the native fp8 tile measured 6-20% slower on every fp8
-  // projection, so that tile keeps two whole stages.)
-  static constexpr bool WRING = MODE == 0 && TM == 256;
+  // TM = 256 (bf16 and native fp8): the weight part of a stage has three
+  // buffers and the activation part two (the weights are requested two stages
+  // ahead), 160 KiB, under the two-group schedule.
+  static constexpr bool WRING = MODE != 1 && TM == 256;
   static constexpr int LDS_BYTES = WRING ? 3 * TN * KB + 2 * TM * KB : STAGES * STAGE_BYTES;
   static constexpr int DPW = STAGE_BYTES / 1024 / NWAVES;            // 1 KiB wave loads per stage
   static constexpr int RPB = 1024 / KB;                              // LDS rows per 1 KiB block
@@ -301,14 +300,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     }
   };
 
-  if constexpr (MODE == 0 && TM == 256) {
+  if constexpr (MODE != 1 && TM == 256) {
     // Two groups of four waves (A = waves 0..3, B = waves 4..7; one of each
     // per SIMD) run half a stage apart: while one wave of a SIMD issues the 64
     // products of a stage back to back, the other reads its operands of the
     // stage from LDS, and at each barrier they swap.  B starts one barrier
     // late; every barrier is shared by both groups.
     //   A: M0 | C0 | M1 | C1 ...      B: - | M0 | C0 | M1 ...
-    // M(t) reads stage t into registers; C(t) runs its products.  The weight
+    // M(t) reads stage t into registers; C(t) runs its products (bf16: two
+    // 32-wide k-steps; native fp8: one 128-wide k-step).  The weight
     // half of stage t sits in weight buffer t % 3, the activation half in
     // activation buffer t % 2 (3 x 32 + 2 x 32 KiB = 160 KiB).
     // Each wave loads one 64-row quarter of one operand (8 wave loads per
@@ -326,6 +326,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     const bool w_loader = grp_b;
     const int quarter = wave_u & 3;
     u32x4 wo0[WA], xo0[4], wo1[WA], xo1[4];
+    i32x8_t wo8[NATIVE8 ? WA : 1], xo8[NATIVE8 ? 4 : 1];
     constexpr int WBUF = TN * KB, XBUF = TM * KB;
     uint8_t* const wring = smem;
     uint8_t* const xring = smem + 3 * WBUF;
@@ -344,6 +345,32 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     // operands of k-step h of stage kt, from the two rings
     auto read_ring = [&](int kt, int h, u32x4(&wo)[WA], u32x4(&xo)[4]) {
       read_ops2(wring + (kt % 3) * WBUF, xring + (kt % 2) * XBUF, h, wo, xo);
+    };
+    // native fp8: the stage's one 128-wide k-step, 32 bytes per lane and tile
+    auto read_ring8 = [&](int kt) {
+      const uint8_t* w = wring + (kt % 3) * WBUF;
+      const uint8_t* x = xring + (kt % 2) * XBUF;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int row = wm * 64 + 16 * c + i16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(x + swz<KB, true>(row, 2 * grp));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(x + swz<KB, true>(row, 2 * grp + 1));
+        xo8[c] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int a = 0; a < WA; ++a) {
+        const int row = wn * WN + 16 * a + i16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(w + swz<KB, true>(row, 2 * grp));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(w + swz<KB, true>(row, 2 * grp + 1));
+        wo8[a] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    };
+    auto mma8 = [&]() {
+#pragma unroll
+      for (int a = 0; a < WA; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wo8[a], xo8[c], acc[a][c], 0, 0, 0, 127, 0, 127);
     };
     if (nk > 0) {
       dma_q(0);
@@ -370,14 +397,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       const int ahead = w_loader ? kt + 2 : kt + 1;
       const bool issued = ahead < nk;
       if (issued) dma_q(ahead);
-      const bool pf = w_loader && P.silu && kt + PF < nk;
+      const bool pf = MODE == 0 && w_loader && P.silu && kt + PF < nk;
       unsigned pf0 = 0;
       if (pf) {
         const uint32_t koffp = (uint32_t)(kt0 + kt + PF) * KT_BYTES;
         pf0 = __builtin_amdgcn_raw_buffer_load_b32(wview, (uint32_t)(l * kbytes), run + koffp, 0);
       }
-      read_ring(kt, 0, wo0, xo0);
-      read_ring(kt, 1, wo1, xo1);
+      if constexpr (NATIVE8) {
+        read_ring8(kt);
+      } else {
+        read_ring(kt, 0, wo0, xo0);
+        read_ring(kt, 1, wo1, xo1);
+      }
       wait_lds_reads();
       // B: the weights of stage kt + 1 have landed (stage kt + 2's 8 loads
       // and this stage's prefetch may still be in flight)
@@ -395,8 +426,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // C(kt)
-      mma(wo0, xo0);
-      mma(wo1, xo1);
+      if constexpr (NATIVE8) {
+        mma8();
+      } else {
+        mma(wo0, xo0);
+        mma(wo1, xo1);
+      }
       // A: the activations of stage kt + 1 have landed
       if (!w_loader) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
       __builtin_amdgcn_sched_barrier(0);
@@ -446,7 +481,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       if (g + 1 < steps) step(g + 1, w1, x1, w0, x0);
     }
   } else if constexpr (MODE == 2) {
-    // Stages kt .. kt + STAGES - 2 are in flight when tile kt's products start;
+    // (128-row fp8 tile) Stages kt .. kt + STAGES - 2 are in flight when tile
+    // kt's products start;
     // one barrier per k-tile both publishes tile kt and retires every wave's
     // reads of the buffer that the next load overwrites.
     const int pre = nk < STAGES - 1 ? nk : STAGES - 1;
