@@ -759,24 +759,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   finish<KVT, D>(P, A, r, g);
 }
 
-// Chunked mode: one wave per (row, page chunk, kv head), four chunks of one
-// row per workgroup (rows x ceil(max_ch / 4) x kv heads workgroups, the kv
-// heads innermost in dispatch order: measured 4% faster than kv-head-major on
-// the 0.6B mixed step, whose kv heads' blocks lie side by side).  Waves past
+// Chunked mode: one wave per (row, page chunk, kv head); a workgroup is four
+// kv heads of one (row, chunk), whose blocks lie side by side in every page,
+// rows x chunks x ceil(n_kv / 4) workgroups (chunk_wg), the kv-head quads
+// innermost in dispatch order, then the chunks, then the rows.  Waves past
 // the row's chunks, or whose row a shared tile covers, exit at once: the grid
-// maps units directly, with no counter to contend on.  A row with one chunk is
-// finished here; the others leave (m, l, O) at record (row, chunk) for the
+// maps units directly, with no counter to contend on; the chunks past a short
+// row's last are whole workgroups that exit together.  (Four chunks of one
+// row per workgroup, measured on the 0.6B mixed step: 241-243 us cold against
+// 238-240; visiting all rows' first chunks first: 248.)  A row with one chunk
+// is finished here; the others leave (m, l, O) at record (row, chunk) for the
 // ordered merge.  A refused row is reported here (chunk 0, kv head 0) and
 // zeroed by the merge.
 //   FUSE: every sequence has one row in the launch; the wave of the row's last
 //   chunk (the one holding its own page) also appends the row's token, as in
 //   the direct kernel, and no other chunk reads that page.
 template <int KVT, int D, bool FUSE>
-__device__ __forceinline__ void chunked_unit(const AttnParams& P, int bx, int by) {
+__device__ __forceinline__ void chunked_unit(const AttnParams& P, int wg) {
   using GE = Geo<KVT, D>;
-  const int cw = (P.max_ch + 3) / 4;
-  const int r = bx / cw, c = 4 * (bx % cw) + (threadIdx.x >> 6), g = by;
-  if (c >= P.max_ch) return;
+  const int nq4 = (P.n_kv + 3) / 4;
+  const int g = 4 * (wg % nq4) + (threadIdx.x >> 6);
+  const int c = (wg / nq4) % P.max_ch, r = wg / nq4 / P.max_ch;
+  if (c >= P.max_ch || g >= P.n_kv) return;
   const int l = lane_id(), grp = l >> 4, n = l & 15;
   const int s = P.seq[r], p = P.pos[r];
   const int npg = (p + kPage) / kPage;
@@ -824,10 +828,7 @@ __device__ __forceinline__ void chunked_unit(const AttnParams& P, int bx, int by
 
 template <int KVT, int D, bool FUSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunked_kernel(AttnParams P) {
-  // workgroups in dispatch order take the kv heads of one (row, chunk group)
-  // in turn: their blocks lie side by side in every page
-  const int i = blockIdx.y * gridDim.x + blockIdx.x;
-  chunked_unit<KVT, D, FUSE>(P, i / P.n_kv, i % P.n_kv);
+  chunked_unit<KVT, D, FUSE>(P, blockIdx.x);
 }
 
 // Shared tiles (prompt slices): one workgroup of NW waves per (tile, page
@@ -1034,8 +1035,7 @@ __global__ __launch_bounds__(64 * kTileWaves) __attribute__((amdgpu_waves_per_eu
   if ((int)blockIdx.x < n_tile_wgs) {
     tile_unit<KVT, D>(P, blockIdx.x, n_tiles, n_units);
   } else {
-    const int i = blockIdx.x - n_tile_wgs;
-    chunked_unit<KVT, D, false>(P, i / P.n_kv, i % P.n_kv);
+    chunked_unit<KVT, D, false>(P, blockIdx.x - n_tile_wgs);
   }
 }
 
@@ -1265,9 +1265,9 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
     else hipLaunchKernelGGL((attn_direct_kernel<KVT, D, true, false>), quads, dim3(256), 0, st, P);
     return;
   }
-  const dim3 chunk_grid(a.n_rows * ((n_ch + 3) / 4), n_kv);
+  const unsigned chunk_wg = (unsigned)(a.n_rows * n_ch * ((n_kv + 3) / 4));  // chunked_unit's workgroups
   if (chunk && a.k_new && a.distinct) {
-    hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, true>), chunk_grid, dim3(256), 0, st, P);
+    hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, true>), dim3(chunk_wg), dim3(256), 0, st, P);
     launch_merge<D>(P, units * P.G, st);
     return;
   }
@@ -1280,10 +1280,10 @@ static void launch_all(const AttnParams& P, const AttnArgs& a, const AttnWs& w, 
   }
   if (n_tiles) {
     const int n_units = n_ch * n_kv, n_tile_wgs = 8 * ((n_units + 7) / 8) * n_tiles;
-    hipLaunchKernelGGL((attn_tiles_rows_kernel<KVT, D>), dim3(n_tile_wgs + chunk_grid.x * n_kv), dim3(256), 0, st, P,
+    hipLaunchKernelGGL((attn_tiles_rows_kernel<KVT, D>), dim3(n_tile_wgs + chunk_wg), dim3(256), 0, st, P,
                        n_tile_wgs, n_tiles, n_units);
   } else {
-    hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), chunk_grid, dim3(256), 0, st, P);
+    hipLaunchKernelGGL((attn_chunked_kernel<KVT, D, false>), dim3(chunk_wg), dim3(256), 0, st, P);
   }
   launch_merge<D>(P, units * P.G, st);
 }
