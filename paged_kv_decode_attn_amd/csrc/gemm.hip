@@ -185,16 +185,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     const int j = n0 / 2 + (WN / 2) * slab + q0 % (WN / 2);
     return q0 < WN / 2 ? j : P.N / 2 + j;
   };
-  auto dma_issue = [&](int kt) {  // stage kt (local index) into buffer kt % STAGES
+  // stage kt (local index) into buffer kt % STAGES: this wave's loads i0 .. i1 - 1
+  auto dma_part = [&](int kt, int i0, int i1) {
     uint8_t* base = smem + (kt % STAGES) * SB + DPW * 1024 * wave_u;
     const uint32_t koff = (uint32_t)(kt0 + kt) * KT_BYTES;
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int b = DPW * wave_u + i;
       const uint32_t soff = (uint32_t)block_row(b) * (uint32_t)kbytes + koff;
       lds_load16(RPB * b < TN ? wview : xview, voff, soff, base + 1024 * i);
     }
   };
+  auto dma_issue = [&](int kt) { dma_part(kt, 0, DPW); };
   // register path (mode 1): thread t moves fp8 chunks q = t + 512 j (j < NR),
   // row q / 4, 16-byte chunk q % 4 of the 64-byte k-tile.
   constexpr int NR = (TN + TM) / 128;
@@ -472,11 +474,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
         refill = kt + STAGES < nk;
       }
       mma(wc, xc);
-      // the refill of stage kt's buffer is issued behind this step's products
-      // (a load issue can stall while the memory pipeline is full; issued
-      // before the products, measured 560-870 clocks per stage boundary with
-      // the matrix core idle)
-      if (refill) dma_issue(kt + STAGES);
+      // The refill of stage kt's buffer is issued behind the products, half
+      // after this boundary step's and half after the next step's (a load
+      // issue can stall while the memory pipeline is full; issued before the
+      // products, measured 560-870 clocks per stage boundary with the matrix
+      // core idle).  Stage order is kept, so the waits above still count
+      // whole later stages.
+      if (refill) dma_part(kt + STAGES, 0, DPW / 2);
+      if (h == 0 && kt > 0 && kt - 1 + STAGES < nk) dma_part(kt - 1 + STAGES, DPW / 2, DPW);
 #pragma unroll
       for (int a = 0; a < WA; ++a) asm volatile("" : "+v"(wn_[a]));
 #pragma unroll
