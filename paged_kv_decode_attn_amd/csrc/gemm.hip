@@ -385,26 +385,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
     }
     lds_barrier();
     if (grp_b) lds_barrier();
-    // Stacked gate/up matrices: the weight loaders also request the weight
-    // lines of stage t + PF into L2 (one dword per lane of their 64-row run),
-    // so that stage's loads into LDS find them there.  The values are folded
-    // into pf_acc, read once a later wait has retired them, and consumed after
-    // the loop under a condition that never holds.  Measured: gate/up 3-9%
-    // faster at batches 256 to 4,096; on the down and qkv shapes the same
-    // prefetch cost 3-4%, so it is used for silu-pair matrices only.
-    constexpr int PF = 6;
-    unsigned pf_acc = 0, pf_prev = 0;
+    // (An L2 prefetch of the weight lines six stages ahead, one dword per lane
+    // of each weight loader's run, had made gate/up 3-9% faster while group A
+    // issued every load; with the loads split over both groups it made gate/up
+    // 4-6% slower at batches 768 and 4,096 and was removed.)
     for (int kt = 0; kt < nk; ++kt) {
       // M(kt)
       const int ahead = w_loader ? kt + 2 : kt + 1;
       const bool issued = ahead < nk;
       if (issued) dma_q(ahead);
-      const bool pf = MODE == 0 && w_loader && P.silu && kt + PF < nk;
-      unsigned pf0 = 0;
-      if (pf) {
-        const uint32_t koffp = (uint32_t)(kt0 + kt + PF) * KT_BYTES;
-        pf0 = __builtin_amdgcn_raw_buffer_load_b32(wview, (uint32_t)(l * kbytes), run + koffp, 0);
-      }
       if constexpr (NATIVE8) {
         read_ring8(kt);
       } else {
@@ -412,18 +401,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
         read_ring(kt, 1, wo1, xo1);
       }
       wait_lds_reads();
-      // B: the weights of stage kt + 1 have landed (stage kt + 2's 8 loads
-      // and this stage's prefetch may still be in flight)
+      // B: the weights of stage kt + 1 have landed (stage kt + 2's 8 loads may
+      // still be in flight)
       if (w_loader) {
-        if (issued) {
-          if (pf) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(9));
-          else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(8));
-        } else {
-          __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
-        }
+        if (issued) __builtin_amdgcn_s_waitcnt(PKD_VMCNT(8));
+        else __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
       }
-      pf_acc ^= pf_prev;
-      pf_prev = pf0;
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -441,9 +424,6 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams P) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!grp_b) lds_barrier();
-    __builtin_amdgcn_s_waitcnt(PKD_VMCNT(0));
-    pf_acc ^= pf_prev;
-    if (pf_acc == 0x9e3779b9u && P.M < 0) reinterpret_cast<float*>(P.y)[0] = 0.f;
   } else if constexpr (MODE == 0) {
     // Ping-pong over the KS = KB / 64 k-steps of each stage: the operands of
     // step g + 1 are read into one register set while the products of step g
