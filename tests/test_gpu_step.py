@@ -65,20 +65,32 @@ def test_tiny_f32_attention_only(H, orc):
 
 def _step_from_public_calls(H, w, layer, pool):
     """The step composed from the public calls, x rounded to bf16 by torch (RNE)
-    before the QKV projection: the path decode_step takes when the projection
-    family cannot round x itself."""
+    before the QKV projection (by the norm-factor call when the layer has
+    norms): the path decode_step takes when the projection family cannot round
+    x itself.  Each matrix-core projection split along K runs its finish pass
+    here."""
     import paged_kv_decode_attn_amd as pkd
     L = layer.layer
     n, D, nq, nkv, d, F = w.n_rows, w.hidden, w.n_q, w.n_kv, w.head_dim, w.ffn
     x = w.x.cuda().contiguous()
     bf = torch.int16
-    xb = x.to(torch.bfloat16).view(bf).contiguous()
+    s, p = H.rows_tensors(w.seq, w.pos)
+    inv_x = inv_h = cs = None
+    if w.norm:
+        inv_x = torch.empty((n,), dtype=torch.float32, device="cuda")
+        xb = torch.empty((n, D), dtype=bf, device="cuda")
+        pkd.rms_norm_factor(x, n, D, w.norm_eps, inv_x, x_bf16=xb)
+    else:
+        xb = x.to(torch.bfloat16).view(bf).contiguous()
+    if w.rope:
+        cs = torch.empty((n, d // 2, 2), dtype=torch.float32, device="cuda")
+        pkd.rope_table(p, n, d, w.rope_base, cs)
+    rope_kw = dict(rope_cs=cs, rope_cols=(nq + nkv) * d, rope_head_dim=d) if w.rope else {}
     ws = lambda M: H.aligned_empty(max(pkd.pkd_gemv_workspace_bytes(M, n), 1))
     qkv = torch.empty((n, (nq + 2 * nkv) * d), dtype=bf, device="cuda")
-    pkd.gemv_rows(L.w_qkv, xb, wl.BF16, n, qkv, wl.BF16, ws=ws(L.w_qkv))
+    pkd.gemv_rows(L.w_qkv, xb, wl.BF16, n, qkv, wl.BF16, ws=ws(L.w_qkv), row_scale=inv_x, **rope_kw)
     q3 = qkv.view(n, nq + 2 * nkv, d)
     q, k, v = (q3[:, :nq].contiguous(), q3[:, nq:nq + nkv].contiguous(), q3[:, nq + nkv:].contiguous())
-    s, p = H.rows_tensors(w.seq, w.pos)
     rows = pkd.make_rows(s, p, len(set(w.seq.tolist())) == n)
     att = torch.empty((n, nq * d), dtype=bf, device="cuda")
     pkd.paged_attn_decode(pool.handle, rows, nq, q, k, v, att, wl.BF16,
@@ -86,8 +98,11 @@ def _step_from_public_calls(H, w, layer, pool):
     h = torch.empty((n, D), dtype=torch.float32, device="cuda")
     hb = torch.empty((n, D), dtype=bf, device="cuda")
     pkd.gemv_rows(L.w_o, att, wl.BF16, n, h, wl.F32, residual=x, y_bf16=hb, ws=ws(L.w_o))
+    if w.norm:
+        inv_h = torch.empty((n,), dtype=torch.float32, device="cuda")
+        pkd.rms_norm_factor(h, n, D, w.norm_eps, inv_h)
     a = torch.empty((n, F), dtype=bf, device="cuda")
-    pkd.gemv_rows(L.w_gate_up, hb, wl.BF16, n, a, wl.BF16, silu_pair=True, ws=ws(L.w_gate_up))
+    pkd.gemv_rows(L.w_gate_up, hb, wl.BF16, n, a, wl.BF16, silu_pair=True, ws=ws(L.w_gate_up), row_scale=inv_h)
     y = torch.empty((n, D), dtype=torch.float32, device="cuda")
     pkd.gemv_rows(L.w_down, a, wl.BF16, n, y, wl.F32, residual=h, ws=ws(L.w_down))
     torch.cuda.synchronize()
@@ -106,6 +121,35 @@ def test_step_vector_family_rounds_x_in_load(H, name, kw):
     layer = H.GpuLayer(w)
     y_step = layer.step(H.GpuPool(w), w.seq, w.pos, w.x)
     y_calls = _step_from_public_calls(H, w, layer, H.GpuPool(w))
+    assert torch.equal(y_step, y_calls)
+
+
+@pytest.mark.parametrize("name,kw,hint,norm_rope", [
+    # chunked pool, rows of one sequence: separate append kernel, then the chunk units
+    ("0.6b-mixed-bf16", dict(n_decode=20, chunk_rows=6, chunk=4, long_max=1200, family=wl.MFMA), 8, False),
+    ("0.6b-mixed-bf16", dict(n_decode=20, chunk_rows=6, chunk=4, long_max=1200, family=wl.MFMA), 8, True),
+    # one row, chunked pool: the append inside the last chunk's unit
+    ("0.6b-b1-bf16", dict(family=wl.MFMA), 8, True),
+    # whole-row units with the shared-prefix staging and the append inside
+    ("7b-b768-prefix-bf16", dict(n=64), 64, True),
+    # shared tiles of a prompt slice
+    ("prefill-chunk", dict(layer="0.6b", p0=1024, n=256), 256, True),
+])
+def test_step_equals_public_calls_matrix_core(H, name, kw, hint, norm_rope):
+    """decode_step with matrix-core projections split along K (each followed
+    by its ordered finish pass), with and without the norm factors and rotary
+    positions, gives the bits of the same step composed from the public calls
+    (gemv_rows, rms_norm_factor, rope_table, paged_attn_decode), on every
+    attention path: chunk units with a separate append, chunk units with the
+    append inside, whole-row units with shared-prefix staging, shared tiles."""
+    w = wl.make(name, "cuda" if name.startswith("7b") else "cpu", **kw)
+    if norm_rope:
+        w = wl.with_norm_rope(w)
+    layer = H.GpuLayer(w, batch_hint=hint)
+    assert layer.layer.w_qkv.k_splits > 1
+    y_step = layer.step(H.GpuPool(w), w.seq, w.pos, w.x)
+    y_calls = _step_from_public_calls(H, w, layer, H.GpuPool(w))
+    assert torch.isfinite(y_step).all()
     assert torch.equal(y_step, y_calls)
 
 
