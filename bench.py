@@ -39,7 +39,10 @@ def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # untimed steps before each timed run: the card reaches its steady clock
+    # after some 20-30 ms of back-to-back steps (a 7B batch-768 step replayed
+    # from a graph: 492 us over the first 20 replays, 420-430 us from the 40th)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="7b-b768-prefix-bf16")
     ap.add_argument("--configs", default="all",
                     help="workloads measured besides the headline one: all, none, or a comma list")
@@ -250,9 +253,11 @@ class Bench:
         return pct(ts)
 
     def graph_steps(self, fn, steps, warmup):
-        """fn captured once in a graph and replayed: every replay between
-        events (median, p10, p90, mean in us; the mean spans the replays
-        back to back)."""
+        """fn captured once in a graph and replayed (us): the mean over `steps`
+        replays back to back with an event before the first and after the
+        last only (an event recorded between replays costs several us of its
+        own), then the median, p10 and p90 of as many more replays, each
+        between two events."""
         torch = self.torch
         gs = self.gstream
         gs.wait_stream(self.stream)
@@ -263,6 +268,11 @@ class Bench:
                 fn(gs)
             for _ in range(warmup):
                 g.replay()
+            e0, e1 = self.ev(), self.ev()
+            e0.record(gs)
+            for _ in range(steps):
+                g.replay()
+            e1.record(gs)
             evs = [self.ev() for _ in range(steps + 1)]
             evs[0].record(gs)
             for i in range(steps):
@@ -270,7 +280,7 @@ class Bench:
                 evs[i + 1].record(gs)
         torch.cuda.synchronize()
         ts = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)]
-        mean = evs[0].elapsed_time(evs[-1]) * 1e3 / steps
+        mean = e0.elapsed_time(e1) * 1e3 / steps
         med, p10, p90 = pct(ts)
         del g
         return med, p10, p90, mean
